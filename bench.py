@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of FP8 MLA context prefill on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input that is
+already resident in HBM: the one-launch static quantizer over Q, K and V,
+then the FP8 varlen prefill (the 32K-token causal workload is a single
+segment, so there is nothing to merge). The headline value is causal-counted
+TFLOP/s of the step: 640 FLOP per visible (query, key) pair and head, with
+640 = 2 * (192 + 128).
+
+Prints ONE JSON line on stdout. Everything else goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal TFLOP/s + % FP8 MFMA peak, MLA D192/V128 12-head varlen prefill"
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, published
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+FLOP_PER_PAIR = 2 * (192 + 128)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_mla_context_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_hash: str):
+    """HBM bytes per prefill launch from committed PMC counters, if they were taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "prefill_c3_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, codes_np, ds, n_rows: int, seed: int = 1):
+    """The oracle, as it stands, on a bounded sample of the workload's query rows."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(wl.total_q, size=n_rows, replace=False))
+    t0 = time.perf_counter()
+    oracle.attention_rows(codes_np[0], codes_np[1], codes_np[2], wl.cu_seqlens_q,
+                          wl.cu_seqlens_k, ds[0], ds[1], ds[2], wl.softmax_scale, wl.causal, rows)
+    dt = time.perf_counter() - t0
+    # visible keys of each sampled row (single causal sequence, Lq == Lk)
+    lq = wl.total_q
+    lk = wl.total_k
+    vis = np.minimum(lk, rows + (lk - lq) + 1) if wl.causal else np.full(n_rows, lk)
+    flop = float(np.sum(vis)) * wl.q.shape[1] * FLOP_PER_PAIR
+    return {
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{n_rows} seeded query rows x {wl.q.shape[1]} heads of {wl.name}, fp64 NumPy "
+                  f"oracle attention on the dequantized FP8 inputs, {dt:.1f} s",
+        "seconds": dt,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C3")
+    ap.add_argument("--cpu-rows", type=int, default=384, help="query rows for the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads or context segments would shard with no or one exchange step).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    from fp8_mla_context_amd import binding as B
+    from synth import make_workload
+
+    B.lib()  # fail loudly if the library is missing
+    t_gen = time.perf_counter()
+    wl = make_workload(args.workload)
+    heads = wl.q.shape[1]
+    log(f"[bench] workload {wl.name}: {wl.description}; generated in "
+        f"{time.perf_counter() - t_gen:.1f} s")
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    # static scale setup (untimed): device amax over the calibration draw, descale = amax / 448
+    descales = []
+    for c in wl.calib():
+        amax = B.amax_per_head(dev_bf16(c)).cpu().numpy()
+        d = B.descale_from_amax_host(amax)
+        B.check_descales_host(d)
+        descales.append(torch.from_numpy(d).cuda())
+    wl._calib = None
+
+    q, k, v = dev_bf16(wl.q), dev_bf16(wl.k), dev_bf16(wl.v)
+    codes = [torch.empty(x.shape, dtype=torch.uint8, device="cuda") for x in (q, k, v)]
+    cu_q = torch.from_numpy(wl.cu_seqlens_q).cuda()
+    cu_k = torch.from_numpy(wl.cu_seqlens_k).cuda()
+    out = torch.empty((wl.total_q, heads, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((heads, wl.total_q), dtype=torch.float32, device="cuda")
+
+    def quant():
+        B.quant_static([q, k, v], descales, outs=codes)
+
+    def prefill():
+        B.prefill_varlen(codes[0], codes[1], codes[2], cu_q, cu_k, wl.max_seqlen_q,
+                         wl.max_seqlen_k, descales[0], descales[1], descales[2], wl.softmax_scale,
+                         wl.causal, out=out, lse=lse)
+
+    def step():
+        quant()
+        prefill()
+
+    pairs = wl.visible_pairs()
+    flop = float(pairs) * heads * FLOP_PER_PAIR
+    quant_bytes = 3 * (wl.q.size + wl.k.size + wl.v.size)  # 2 B read + 1 B written per element
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    # timed region: exactly `steps` steps, synchronized on both sides
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    value = flop / (wall / args.steps) / 1e12
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    # per-kernel durations with HIP events on the launch stream (torch's current stream)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record(stream)
+        quant()
+        e[1].record(stream)
+        prefill()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    prefill_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    prefill_min = float(np.min([e[1].elapsed_time(e[2]) for e in ev]))
+    achieved = flop / (prefill_ms * 1e-3) / 1e12
+    log(f"[bench] event timing: quant {quant_ms * 1e3:.1f} us ({quant_bytes / quant_ms / 1e6:.0f} GB/s), "
+        f"prefill {prefill_ms:.3f} ms (min {prefill_min:.3f}) = {achieved:.1f} TFLOP/s")
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {n} bytes read + {n} bytes written per copy, 3 copies")
+
+    khash = kernel_source_hash()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {wl.description}",
+            "tokens": wl.total_q, "heads": heads, "head_dim_qk": 192, "head_dim_v": 128,
+            "causal": bool(wl.causal), "causal_flop": flop,
+            "step": "quant_static(Q,K,V) + prefill_varlen",
+        },
+        "pct_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
+        "kernels": {
+            "quant_static_us": round(quant_ms * 1e3, 2),
+            "quant_static_GBps": round(quant_bytes / quant_ms / 1e6, 1),
+            "prefill_ms": round(prefill_ms, 4),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_fp8_kernel",
+            "achieved": round(achieved, 2),
+            "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+            "traffic": load_traffic(khash),
+        },
+        "kernel_hash": khash,
+    }
+
+    if not args.no_cpu_baseline:
+        codes_np = [c.cpu().numpy() for c in codes]
+        ds_np = [d.cpu().numpy() for d in descales]
+        log("[bench] timing the CPU oracle on a sample ...")
+        cb = cpu_baseline(wl, codes_np, ds_np, args.cpu_rows)
+        log(f"[bench] cpu oracle: {cb['value'] * 1e3:.2f} GFLOP/s on {cb['cores']} threads, "
+            f"{cb['seconds']:.1f} s")
+        result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

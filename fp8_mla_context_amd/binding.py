@@ -1,0 +1,227 @@
+"""Thin Python binding of libmla_fp8.so (ctypes).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream. If the library is not
+built this module raises on first use; there is no fallback path.
+
+Names mirror the C ABI in ``include/mla_fp8.h``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+from .build import LIB_PATH
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARGUMENT = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_HIP = 3
+
+D_QK = 192
+D_V = 128
+
+_c_i32 = ctypes.c_int32
+_c_i64 = ctypes.c_int64
+_c_vp = ctypes.c_void_p
+_c_fp = ctypes.POINTER(ctypes.c_float)
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)}: {last_error()}")
+        self.status = status
+
+
+class QuantJob(ctypes.Structure):
+    _fields_ = [
+        ("x", _c_vp),
+        ("stride_token", _c_i64),
+        ("stride_head", _c_i64),
+        ("n_tokens", _c_i64),
+        ("head_dim", _c_i32),
+        ("descale", _c_vp),
+        ("y", _c_vp),
+    ]
+
+
+_LIB = None
+
+# exported symbol -> (restype, argtypes)
+SIGNATURES = {
+    "mla_abi_version": (ctypes.c_int, []),
+    "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mla_last_error": (ctypes.c_char_p, []),
+    "mla_fp8_quant_static": (ctypes.c_int, [ctypes.POINTER(QuantJob), _c_i32, _c_i32, _c_vp]),
+    "mla_fp8_amax_per_head": (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp,
+                                             _c_vp]),
+    "mla_fp8_prefill_varlen": (ctypes.c_int, [
+        _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32,
+        _c_i32, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "mla_merge_lse": (ctypes.c_int, [
+        _c_i32, ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp), _c_i64, _c_i64, _c_i32, _c_i32, _c_vp,
+        _c_vp, _c_i64, _c_vp]),
+    "mla_check_descales_host": (ctypes.c_int, [_c_fp, _c_i32]),
+    "mla_descale_from_amax_host": (ctypes.c_int, [_c_fp, _c_i32, _c_fp]),
+}
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m fp8_mla_context_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().mla_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().mla_last_error().decode()
+
+
+def _check(status: int, what: str):
+    if status != MLA_OK:
+        raise MlaError(status, what)
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+# --------------------------------------------------------------------------- host helpers
+
+def check_descales_host(descale: np.ndarray) -> None:
+    d = np.ascontiguousarray(descale, dtype=np.float32)
+    _check(lib().mla_check_descales_host(d.ctypes.data_as(_c_fp), d.shape[0]),
+           "mla_check_descales_host")
+
+
+def descale_from_amax_host(amax: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(amax, dtype=np.float32)
+    out = np.empty_like(a)
+    _check(lib().mla_descale_from_amax_host(a.ctypes.data_as(_c_fp), a.shape[0],
+                                            out.ctypes.data_as(_c_fp)),
+           "mla_descale_from_amax_host")
+    return out
+
+
+# --------------------------------------------------------------------------- device ops
+
+def amax_per_head(x, stream=None):
+    """x: bf16 [T, H, D] (last dim contiguous). Returns fp32 [H] on x's device."""
+    import torch
+
+    assert x.dtype == torch.bfloat16 and x.dim() == 3 and x.stride(2) == 1
+    amax = torch.empty(x.shape[1], dtype=torch.float32, device=x.device)
+    _check(lib().mla_fp8_amax_per_head(_ptr(x), x.stride(0), x.stride(1), x.shape[0], x.shape[1],
+                                       x.shape[2], _ptr(amax), _stream(stream)),
+           "mla_fp8_amax_per_head")
+    return amax
+
+
+def quant_static(xs: Sequence, descales: Sequence, outs: Optional[Sequence] = None, stream=None):
+    """Quantize 1..3 bf16 tensors [T, H, D] (token/head strides allowed, last dim contiguous)
+    with fp32 [H] descales in ONE launch. Returns uint8 E4M3 code tensors [T, H, D]."""
+    import torch
+
+    if len(xs) != len(descales) or not 1 <= len(xs) <= 3:
+        raise ValueError("need 1..3 tensors and one descale vector each")
+    heads = xs[0].shape[1]
+    jobs = (QuantJob * len(xs))()
+    ys = []
+    for i, (x, d) in enumerate(zip(xs, descales)):
+        if x.dtype != torch.bfloat16 or x.dim() != 3 or x.stride(2) != 1 or x.shape[1] != heads:
+            raise ValueError("x must be bf16 [T, H, D] with a contiguous last dim")
+        if d.dtype != torch.float32 or d.shape != (heads,) or not d.is_contiguous():
+            raise ValueError("descale must be contiguous fp32 [H]")
+        y = outs[i] if outs is not None else torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        if y.dtype != torch.uint8 or tuple(y.shape) != tuple(x.shape) or not y.is_contiguous():
+            raise ValueError("output must be contiguous uint8 with x's shape")
+        jobs[i] = QuantJob(_ptr(x), x.stride(0), x.stride(1), x.shape[0], x.shape[2], _ptr(d),
+                           _ptr(y))
+        ys.append(y)
+    _check(lib().mla_fp8_quant_static(jobs, len(xs), heads, _stream(stream)), "mla_fp8_quant_static")
+    return ys
+
+
+def prefill_varlen(q8, k8, v8, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                   descale_q, descale_k, descale_v, softmax_scale: float, causal: bool,
+                   out=None, lse=None, lse_stride: Optional[int] = None, stream=None):
+    """FP8 varlen attention. q8 [Tq,H,192], k8 [Tk,H,192], v8 [Tk,H,128] uint8 codes (contiguous);
+    cu_seqlens int32 [B+1] on device. Returns (out bf16 [Tq,H,128], lse fp32 [H, lse_stride])."""
+    import torch
+
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8 or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError("q8/k8/v8 must be contiguous uint8 [T, H, D]")
+    for t in (cu_seqlens_q, cu_seqlens_k):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous int32")
+    tq, heads = q8.shape[0], q8.shape[1]
+    tk = k8.shape[0]
+    if out is None:
+        out = torch.empty((tq, heads, D_V), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse_stride = tq if lse_stride is None else lse_stride
+        lse = torch.empty((heads, lse_stride), dtype=torch.float32, device=q8.device)
+    elif lse_stride is None:
+        lse_stride = lse.stride(0)
+    batch = cu_seqlens_q.shape[0] - 1
+    _check(lib().mla_fp8_prefill_varlen(
+        _ptr(q8), _ptr(k8), _ptr(v8), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
+        int(max_seqlen_q), int(max_seqlen_k), tq, tk, heads, q8.shape[2], v8.shape[2],
+        _ptr(descale_q), _ptr(descale_k), _ptr(descale_v), float(softmax_scale), int(bool(causal)),
+        _ptr(out), _ptr(lse), int(lse_stride), _stream(stream)), "mla_fp8_prefill_varlen")
+    return out, lse
+
+
+def merge_lse(outs: Sequence, lses: Sequence, out=None, lse_out=None, stream=None):
+    """Merge partials: outs bf16 [T,H,128] each, lses fp32 [H, ld] each (same ld)."""
+    import torch
+
+    n = len(outs)
+    if n != len(lses) or n < 1:
+        raise ValueError("need one lse per output")
+    tq, heads = outs[0].shape[0], outs[0].shape[1]
+    ld_in = lses[0].stride(0)
+    for o, l_ in zip(outs, lses):
+        if o.dtype != torch.bfloat16 or tuple(o.shape) != (tq, heads, D_V) or not o.is_contiguous():
+            raise ValueError("outs must be contiguous bf16 [T, H, 128]")
+        if l_.dtype != torch.float32 or l_.stride(0) != ld_in or l_.stride(1) != 1:
+            raise ValueError("lses must be fp32 [H, ld] with one common ld")
+    if out is None:
+        out = torch.empty_like(outs[0])
+    if lse_out is None:
+        lse_out = torch.empty((heads, tq), dtype=torch.float32, device=outs[0].device)
+    op = (_c_vp * n)(*[_ptr(o) for o in outs])
+    lp = (_c_vp * n)(*[_ptr(l_) for l_ in lses])
+    _check(lib().mla_merge_lse(n, op, lp, ld_in, tq, heads, D_V, _ptr(out), _ptr(lse_out),
+                               lse_out.stride(0), _stream(stream)), "mla_merge_lse")
+    return out, lse_out

@@ -1,0 +1,385 @@
+// FP8 varlen context-prefill attention for MLA shapes (Q/K 192, V 128) on gfx950.
+//
+// "[ROCm][MLA] Add guarded gfx942 FP8 context prefill" (vLLM #51551):
+// Background (a packed variable-length kernel for D192 Q/K and D128 V with
+// per-head static FP8 quantization) and "What this PR does" (12 heads, FP8
+// Q/K/V); the close comment separates causal and non-causal shapes.
+//
+// Design (gfx950, wave64):
+//  * One workgroup = 8 waves = 256 query rows of one (sequence, head); each
+//    wave owns 32 rows. Workgroups are ordered heaviest first: the flattened
+//    block index walks query tiles from the last (most keys under a causal
+//    mask) to the first, with heads and sequences fastest.
+//  * K/V tiles of 64 keys are staged in LDS in their natural [key][dim]
+//    layout, double-buffered: the global loads of tile t+1 are issued into
+//    registers before tile t is computed and stored to the other buffer after
+//    it, so one barrier per tile suffices and HBM/L2 latency hides behind the
+//    MFMA work.
+//  * S^T = K * Q^T on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32): the
+//    Q fragment (32 rows x 192) stays in registers as the B operand, K rows
+//    are read from LDS as the A operand. In the 32x32 accumulator layout every
+//    lane then holds one query row (lane % 32) and 32 of the tile's keys, so
+//    the row max needs one cross-lane step (lane ^ 32) and row sums stay per
+//    lane until the end.
+//  * Online softmax in base 2: c = dq*dk*softmax_scale*log2(e) > 0, so the
+//    tile max is taken on raw logits and scaled once; P' = 2^(c*s - m + 8)
+//    is one FMA and one v_exp_f32 per element (pre-scaled by 2^8 so small
+//    weights stay out of E4M3 subnormals). O and l are rescaled only when
+//    some row's running max grew (a wave-uniform branch).
+//  * O^T = V^T * P^T on the same MFMA: P' is split in two E4M3 terms,
+//    hi = E4M3(P') (round to nearest even) and lo = E4M3(P' - hi), both
+//    accumulated into the same fp32 O; one E4M3 term would carry ~2.5%
+//    relative error per weight, which the output tolerance does not allow on
+//    diffuse heads. The accumulator layout of S^T already is the B operand
+//    (lane = query row, bytes = 32 keys). The V^T A operand comes from
+//    ds_read_b64_tr_b8: within each 16-lane group, output lane i receives byte
+//    i % 8 of the 8-byte windows addressed by lanes 2b + i/8 (b = 0..7); with
+//    lanes 2b and 2b+1 pointing at the same key row and at dims d0 and d0 + 8,
+//    lane i gets dim d0 + i of 8 keys, in the key order of the P operand.
+//  * Causal (bottom-right aligned: key j visible to row i iff j <= i + Lk - Lq):
+//    a wave skips tiles past its last visible key; only tiles that cross the
+//    diagonal or the ragged end are masked element-wise.
+//  * Epilogue: out = O * dv / l in bf16, lse = ln2 * (m + log2 l - 8).
+#include "mla_internal.h"
+
+namespace {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+constexpr int kDqk = 192;
+constexpr int kDv = 128;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+constexpr int kBN = 64;           // keys per tile
+constexpr int kKStride = 208;     // LDS bytes per K row: 192 + 16 (8 consecutive rows hit distinct banks)
+constexpr int kVStride = 144;     // LDS bytes per V row: 128 + 16
+constexpr int kKTile = kBN * kKStride;
+constexpr int kVTile = kBN * kVStride;
+constexpr int kKChunks = kBN * kDqk / 16;  // 768 16-byte chunks per K tile
+constexpr int kVChunks = kBN * kDv / 16;   // 512 per V tile
+constexpr float kLn2 = 0.69314718055994530942f;
+
+struct PrefillParams {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const float* dq;
+  const float* dk;
+  const float* dv;
+  uint16_t* out;
+  float* lse;
+  int64_t lse_stride;
+  int64_t total_q;
+  int64_t total_k;
+  int32_t batch;
+  int32_t n_heads;
+  int32_t n_m_tiles;
+  int32_t causal;
+  float scale_log2;
+};
+
+__device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
+  // cbsz = blgp = 0: both operands E4M3; zero scales select the unscaled instruction
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v8i load32(const uint8_t* p) {
+  const v4i a = *reinterpret_cast<const v4i*>(p);
+  const v4i b = *reinterpret_cast<const v4i*>(p + 16);
+  return v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+}
+
+__device__ __forceinline__ v2i read_tr8(const uint8_t* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) v2i*)(lds_ptr));
+}
+
+// Splits four weights into E4M3 hi/lo terms, packed 4 per dword.
+__device__ __forceinline__ void split_pack4(float p0, float p1, float p2, float p3, int& hw,
+                                            int& lw) {
+  hw = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+  hw = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, hw, true);
+  const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+  const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+  lw = __builtin_amdgcn_cvt_pk_fp8_f32(p0 - h01.x, p1 - h01.y, 0, false);
+  lw = __builtin_amdgcn_cvt_pk_fp8_f32(p2 - h23.x, p3 - h23.y, lw, true);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (kKTile + kVTile)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int H = p.n_heads;
+
+  // heaviest query tiles first; heads, then sequences, vary fastest
+  int idx = blockIdx.x;
+  const int h = idx % H;
+  idx /= H;
+  const int b = idx % p.batch;
+  idx /= p.batch;
+  const int m_tile = p.n_m_tiles - 1 - idx;
+
+  int64_t q0 = p.cu_q[b], q1 = p.cu_q[b + 1];
+  int64_t k0 = p.cu_k[b], k1 = p.cu_k[b + 1];
+  q0 = min(max(q0, (int64_t)0), p.total_q);
+  q1 = min(max(q1, q0), p.total_q);
+  k0 = min(max(k0, (int64_t)0), p.total_k);
+  k1 = min(max(k1, k0), p.total_k);
+  const int Lq = static_cast<int>(q1 - q0);
+  const int Lk = static_cast<int>(k1 - k0);
+  const int row0 = m_tile * kBM;
+  if (row0 >= Lq) return;  // uniform over the workgroup
+  const int off = Lk - Lq;
+  const bool causal = p.causal != 0;
+  int kend = Lk;
+  if (causal) kend = min(Lk, max(0, min(Lq, row0 + kBM) + off));
+
+  const int g = lane >> 5;
+  const int col = lane & 31;
+  const int wrow0 = row0 + wave * 32;
+  const int my_row = wrow0 + col;
+  const bool row_ok = my_row < Lq;
+  const bool wave_active = wrow0 < Lq;
+  int wave_kend = kend;
+  if (causal) wave_kend = min(Lk, max(0, min(Lq, wrow0 + 32) + off));
+
+  const int64_t q_rs = static_cast<int64_t>(H) * kDqk;
+  const int64_t k_rs = static_cast<int64_t>(H) * kDqk;
+  const int64_t v_rs = static_cast<int64_t>(H) * kDv;
+
+  // Q fragment (B operand): row my_row, dims [64*kb + 32*g, +32)
+  v8i qf[3];
+  if (row_ok) {
+    const uint8_t* qp = p.q + (q0 + my_row) * q_rs + h * kDqk + 32 * g;
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) qf[kb] = load32(qp + 64 * kb);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) qf[kb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  const float c = p.dq[h] * p.dk[h] * p.scale_log2;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  v16f o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+
+  const uint8_t* kbase = p.k + k0 * k_rs + h * kDqk;
+  const uint8_t* vbase = p.v + k0 * v_rs + h * kDv;
+
+  // this thread's share of a tile load: K chunks tid and tid + 512 (< 768), V chunk tid
+  const int kr0 = tid / 12, kc0 = tid - 12 * (tid / 12);
+  const int kr1 = (tid + kThreads) / 12, kc1 = (tid + kThreads) - 12 * ((tid + kThreads) / 12);
+  const bool has_k1 = tid + kThreads < kKChunks;
+  const int vr = tid >> 3, vc = tid & 7;
+  v4i kreg0, kreg1, vreg;
+  auto load_tile = [&](int kt) {
+    const v4i z = v4i{0, 0, 0, 0};
+    kreg0 = (kt + kr0 < Lk) ? *reinterpret_cast<const v4i*>(kbase + (kt + kr0) * k_rs + kc0 * 16) : z;
+    kreg1 = (has_k1 && kt + kr1 < Lk)
+                ? *reinterpret_cast<const v4i*>(kbase + (kt + kr1) * k_rs + kc1 * 16)
+                : z;
+    vreg = (kt + vr < Lk) ? *reinterpret_cast<const v4i*>(vbase + (kt + vr) * v_rs + vc * 16) : z;
+  };
+  auto store_tile = [&](int buf) {
+    uint8_t* kl = lds + buf * (kKTile + kVTile);
+    uint8_t* vl = kl + kKTile;
+    *reinterpret_cast<v4i*>(kl + kr0 * kKStride + kc0 * 16) = kreg0;
+    if (has_k1) *reinterpret_cast<v4i*>(kl + kr1 * kKStride + kc1 * 16) = kreg1;
+    *reinterpret_cast<v4i*>(vl + vr * kVStride + vc * 16) = vreg;
+  };
+
+  // transposed-read addresses (see the header): lane -> (16-lane group G, source slot s)
+  const int grp = lane >> 4, slot = lane & 15;
+  const int tb = slot >> 1, tp = slot & 1;
+  int vt_off[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int key = 16 * r + 8 * (tb >> 2) + 4 * (grp >> 1) + (tb & 3);
+    vt_off[r] = key * kVStride + 16 * (grp & 1) + 8 * tp;
+  }
+
+  if (kend > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  int it = 0;
+  for (int kt = 0; kt < kend; kt += kBN, ++it) {
+    const int cur = it & 1;
+    const bool has_next = kt + kBN < kend;
+    if (has_next) load_tile(kt + kBN);
+
+    if (wave_active && kt < wave_kend) {
+      const uint8_t* kl = lds + cur * (kKTile + kVTile);
+      const uint8_t* vl = kl + kKTile;
+      // S^T tile: two 32-key blocks, K-dim 192 = 3 x 64
+      v16f s[2];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[b2][r] = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 3; ++kb) {
+          const v8i a = load32(kl + (32 * b2 + col) * kKStride + 64 * kb + 32 * g);
+          s[b2] = mfma_f8(a, qf[kb], s[b2]);
+        }
+      }
+
+      const bool need_mask = (kt + kBN > Lk) || (causal && kt + kBN - 1 > wrow0 + off);
+      if (need_mask) {
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt + 32 * b2 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key >= Lk || (causal && key > my_row + off)) s[b2][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        mx = fmaxf(mx, fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1])));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * c);  // c > 0; -inf stays -inf
+      if (__any(m_new > m_run)) {
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while m_run is -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m_run = m_new;
+      }
+      const float nbias = 8.0f - ((m_run == -INFINITY) ? 0.f : m_run);
+
+      float lsum = 0.f;
+      v8i phi, plo;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int b2 = w >> 2;
+        const int r0 = 4 * (w & 3);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b2][r0 + 0], c, nbias));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b2][r0 + 1], c, nbias));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(s[b2][r0 + 2], c, nbias));
+        const float p3 = __builtin_amdgcn_exp2f(fmaf(s[b2][r0 + 3], c, nbias));
+        lsum += (p0 + p1) + (p2 + p3);
+        int hw, lw;
+        split_pack4(p0, p1, p2, p3, hw, lw);
+        phi[w] = hw;
+        plo[w] = lw;
+      }
+      l_run += lsum;
+
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint8_t* vp = vl + 32 * db;
+        const v2i r0 = read_tr8(vp + vt_off[0]);
+        const v2i r1 = read_tr8(vp + vt_off[1]);
+        const v2i r2 = read_tr8(vp + vt_off[2]);
+        const v2i r3 = read_tr8(vp + vt_off[3]);
+        const v8i a = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+        o[db] = mfma_f8(a, phi, o[db]);
+        o[db] = mfma_f8(a, plo, o[db]);
+      }
+    }
+
+    if (has_next) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: this lane holds row my_row, dims 32*db + 8*(r/4) + 4*g + r%4
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (row_ok) {
+    const float inv = (l_tot > 0.f) ? p.dv[h] / l_tot : 0.f;
+    uint16_t* op = p.out + (q0 + my_row) * (static_cast<int64_t>(H) * kDv) + h * kDv;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int grp4 = 0; grp4 < 4; ++grp4) {
+        const uint32_t e0 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 0] * inv);
+        const uint32_t e1 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 1] * inv);
+        const uint32_t e2 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 2] * inv);
+        const uint32_t e3 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 3] * inv);
+        *reinterpret_cast<uint2*>(op + 32 * db + 8 * grp4 + 4 * g) =
+            make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+      }
+    if (g == 0 && p.lse != nullptr)
+      p.lse[static_cast<int64_t>(h) * p.lse_stride + q0 + my_row] =
+          (l_tot > 0.f) ? (m_run + __log2f(l_tot) - 8.0f) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+extern "C" int mla_fp8_prefill_varlen(const void* q, const void* k, const void* v,
+                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                      int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                      int64_t total_q, int64_t total_k, int32_t n_heads,
+                                      int32_t head_dim_qk, int32_t head_dim_v,
+                                      const float* descale_q, const float* descale_k,
+                                      const float* descale_v, float softmax_scale, int32_t causal,
+                                      void* out, float* lse, int64_t lse_stride, void* stream) {
+  if (head_dim_qk != kDqk || head_dim_v != kDv)
+    return mla::fail(MLA_ERR_UNSUPPORTED, "head dims %d/%d: only 192/128 are implemented",
+                     head_dim_qk, head_dim_v);
+  if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "negative size");
+  if (n_heads < 1) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "n_heads = %d < 1", n_heads);
+  if (causal != 0 && causal != 1)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "causal = %d is not 0 or 1", causal);
+  if (!(softmax_scale > 0.f) || !(softmax_scale <= 3.4028234663852886e38f))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and positive");
+  if (total_q >= (1ll << 31) || total_k >= (1ll << 31))
+    return mla::fail(MLA_ERR_UNSUPPORTED, "total_q and total_k must be < 2^31");
+  if (total_q == 0 || batch == 0 || max_seqlen_q == 0) return mla::ok();
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr ||
+      descale_q == nullptr || descale_k == nullptr || descale_v == nullptr)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (total_k > 0 && (k == nullptr || v == nullptr))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "k or v is NULL");
+  if (!mla::aligned16(q) || !mla::aligned16(k) || !mla::aligned16(v) || !mla::aligned16(out))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
+  if (lse != nullptr && lse_stride < total_q)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "lse_stride < total_q");
+  const int64_t n_m = (static_cast<int64_t>(max_seqlen_q) + kBM - 1) / kBM;
+  const int64_t blocks = n_m * batch * n_heads;
+  if (blocks >= (1ll << 31)) return mla::fail(MLA_ERR_UNSUPPORTED, "grid too large");
+
+  PrefillParams prm;
+  prm.q = static_cast<const uint8_t*>(q);
+  prm.k = static_cast<const uint8_t*>(k);
+  prm.v = static_cast<const uint8_t*>(v);
+  prm.cu_q = cu_seqlens_q;
+  prm.cu_k = cu_seqlens_k;
+  prm.dq = descale_q;
+  prm.dk = descale_k;
+  prm.dv = descale_v;
+  prm.out = static_cast<uint16_t*>(out);
+  prm.lse = lse;
+  prm.lse_stride = lse_stride;
+  prm.total_q = total_q;
+  prm.total_k = total_k;
+  prm.batch = batch;
+  prm.n_heads = n_heads;
+  prm.n_m_tiles = static_cast<int32_t>(n_m);
+  prm.causal = causal;
+  prm.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  hipLaunchKernelGGL(prefill_fp8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), prm);
+  return mla::check_launch("prefill_fp8_kernel");
+}

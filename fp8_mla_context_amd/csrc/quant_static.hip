@@ -1,0 +1,279 @@
+// Static per-head FP8 (OCP E4M3FN) quantizer and per-head amax calibration.
+//
+// "[ROCm][MLA] Add guarded gfx942 FP8 context prefill" (vLLM #51551), Summary
+// and "What this PR does": static per-head scales replace the runtime amax
+// reduction, and one kernel quantizes the attention inputs. Here one launch
+// covers up to three tensors (Q, K, V) with their own head dims and descales.
+//
+// Rounding contract: the code is the correctly rounded E4M3 value of the exact
+// quotient x / descale (nearest, ties to even, saturating at +-448, NaN kept).
+// The kernel multiplies by r = 1/descale in fp32, which can be off by up to
+// ~3 ulp, then rounds with integer bit operations. Only when the fp32
+// quotient lies within 16 ulp of an E4M3 rounding boundary M can that differ
+// from the exact result; there the sign of x - M*descale is taken in fp64,
+// where M*descale (5 + 24 significant bits) and the difference are exact.
+//
+// HBM-bound: 2 bytes read + 1 byte written per element. Each thread handles
+// 16 consecutive elements of one (token, head) row: two 16-byte loads, one
+// 16-byte store.
+#include "mla_internal.h"
+
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr int kMaxJobs = 3;
+
+struct QuantJobDev {
+  const uint16_t* x;
+  uint8_t* y;
+  const float* descale;
+  int64_t stride_token;
+  int64_t stride_head;
+  uint32_t chunk_begin;  // first global chunk index of this job
+  uint32_t n_chunks;
+  int32_t head_dim;
+  int32_t vec;  // 1: 16-byte loads are aligned
+};
+
+struct QuantParams {
+  QuantJobDev job[kMaxJobs];
+  int32_t n_jobs;
+  uint32_t total_chunks;
+  mla::FastDiv heads;
+};
+
+// One bf16 (bits in the low 16 bits) divided by descale d (r ~ 1/d) to an E4M3 code.
+__device__ __forceinline__ uint32_t quant_one(uint32_t xb, float d, float r) {
+  const uint32_t sign = (xb >> 8) & 0x80u;
+  const uint32_t xa = (xb & 0x7FFFu) << 16;  // |x| as fp32 bits
+  if (xa > 0x7F800000u) return 0x7Fu | sign;  // NaN
+  const float ax = __uint_as_float(xa);
+  const float qf = ax * r;
+  const uint32_t a = __float_as_uint(qf);
+  if (a > 0x43E00000u) return 0x7Eu | sign;  // > 448 (also +Inf): saturate, no boundary nearby
+  uint32_t lower;  // code of the E4M3 value just below (or at) qf
+  bool up, near;
+  float mid;       // the rounding boundary above `lower`
+  if (a >= 0x3C800000u) {  // >= 2^-6: normal E4M3 range
+    lower = (a >> 20) - (120u << 3);
+    const uint32_t low = a & 0xFFFFFu;
+    up = low > 0x80000u;
+    near = (low > 0x80000u ? low - 0x80000u : 0x80000u - low) <= 16u;
+    mid = __uint_as_float((a & ~0xFFFFFu) | 0x80000u);
+  } else {  // subnormal E4M3: multiples of 2^-9
+    const float t = qf * 512.0f;  // exact
+    const float n = floorf(t);
+    const float f = t - n;        // exact
+    lower = static_cast<uint32_t>(n);
+    up = f > 0.5f;
+    near = fabsf(f - 0.5f) <= 0x1p-17f;
+    mid = (n + 0.5f) * 0x1p-9f;  // exact
+  }
+  if (near) {
+    // exact side of the boundary: sign of |x| - mid * d, computed exactly in fp64
+    const double diff = static_cast<double>(ax) - static_cast<double>(mid) * static_cast<double>(d);
+    up = diff > 0.0 || (diff == 0.0 && (lower & 1u));
+  }
+  return (lower + (up ? 1u : 0u)) | sign;
+}
+
+__device__ __forceinline__ uint32_t quant_pack4(uint32_t w0, uint32_t w1, float d, float r) {
+  // w0 holds bf16 elements 0,1 (low, high halves), w1 elements 2,3
+  uint32_t c0 = quant_one(w0 & 0xFFFFu, d, r);
+  uint32_t c1 = quant_one(w0 >> 16, d, r);
+  uint32_t c2 = quant_one(w1 & 0xFFFFu, d, r);
+  uint32_t c3 = quant_one(w1 >> 16, d, r);
+  return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+}
+
+__global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantParams p) {
+  const uint32_t stride = gridDim.x * kQuantThreads;
+  for (uint32_t c = blockIdx.x * kQuantThreads + threadIdx.x; c < p.total_chunks; c += stride) {
+    int j = 0;
+    if (p.n_jobs > 1 && c >= p.job[1].chunk_begin) j = 1;
+    if (p.n_jobs > 2 && c >= p.job[2].chunk_begin) j = 2;
+    const QuantJobDev& jb = p.job[j];
+    const uint32_t local = c - jb.chunk_begin;
+    // chunks per (token, head) row: 12 for D = 192, 8 for D = 128
+    uint32_t row, col;
+    if (jb.head_dim == 192) {
+      row = local / 12u;
+      col = local - row * 12u;
+    } else {
+      row = local >> 3;
+      col = local & 7u;
+    }
+    const uint32_t t = mla::fdiv(row, p.heads);
+    const uint32_t h = row - t * p.heads.d;
+    const float d = jb.descale[h];
+    const float r = 1.0f / d;
+    const uint16_t* src = jb.x + static_cast<int64_t>(t) * jb.stride_token +
+                          static_cast<int64_t>(h) * jb.stride_head + col * 16u;
+    uint32_t w[8];
+    if (jb.vec) {
+      const uint4 a = *reinterpret_cast<const uint4*>(src);
+      const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+      w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w[i] = static_cast<uint32_t>(src[2 * i]) | (static_cast<uint32_t>(src[2 * i + 1]) << 16);
+    }
+    uint4 o;
+    o.x = quant_pack4(w[0], w[1], d, r);
+    o.y = quant_pack4(w[2], w[3], d, r);
+    o.z = quant_pack4(w[4], w[5], d, r);
+    o.w = quant_pack4(w[6], w[7], d, r);
+    *reinterpret_cast<uint4*>(jb.y + static_cast<int64_t>(row) * jb.head_dim + col * 16u) = o;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// amax per head: max |x| over tokens and dims. Float bits of |x| order like
+// unsigned integers, so an integer atomic max is exact and order-independent.
+// NaN inputs (bits above +Inf) win the max and surface as a non-finite amax.
+
+struct AmaxParams {
+  const uint16_t* x;
+  int64_t stride_token;
+  int64_t stride_head;
+  uint32_t* amax_bits;
+  uint32_t n_rows;  // n_tokens * n_heads
+  int32_t head_dim;
+  mla::FastDiv heads;
+};
+
+__global__ __launch_bounds__(kQuantThreads) void zero_words_kernel(uint32_t* p, int n) {
+  int i = blockIdx.x * kQuantThreads + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// One wave per (token, head) row; lanes stride over the row's dims. Each
+// workgroup keeps its running maxima per head in LDS (n_heads <= kAmaxLdsHeads)
+// and publishes them with one global atomic per head at the end.
+constexpr int kAmaxLdsHeads = 1024;
+
+__global__ __launch_bounds__(kQuantThreads) void amax_kernel(AmaxParams p) {
+  __shared__ uint32_t smax[kAmaxLdsHeads];
+  const int H = static_cast<int>(p.heads.d);
+  const bool use_lds = H <= kAmaxLdsHeads;
+  if (use_lds)
+    for (int i = threadIdx.x; i < H; i += kQuantThreads) smax[i] = 0u;
+  __syncthreads();
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t waves = gridDim.x * (kQuantThreads / 64);
+  for (uint32_t row = blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6); row < p.n_rows;
+       row += waves) {
+    const uint32_t t = mla::fdiv(row, p.heads);
+    const uint32_t h = row - t * p.heads.d;
+    const uint16_t* src =
+        p.x + static_cast<int64_t>(t) * p.stride_token + static_cast<int64_t>(h) * p.stride_head;
+    uint32_t m = 0;
+    for (int dd = lane; dd < p.head_dim; dd += 64) m = max(m, (uint32_t)(src[dd] & 0x7FFFu));
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if (lane == 0) {
+      if (use_lds)
+        atomicMax(smax + h, m << 16);
+      else
+        atomicMax(p.amax_bits + h, m << 16);
+    }
+  }
+  __syncthreads();
+  if (use_lds)
+    for (int i = threadIdx.x; i < H; i += kQuantThreads)
+      if (smax[i] != 0u) atomicMax(p.amax_bits + i, smax[i]);
+}
+
+int grid_for(uint64_t work_items, int per_block) {
+  uint64_t blocks = (work_items + per_block - 1) / per_block;
+  const uint64_t cap = 256ull * 16ull;  // 256 CUs x 16 resident blocks of 256 threads
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return static_cast<int>(blocks);
+}
+
+}  // namespace
+
+extern "C" int mla_fp8_quant_static(const mla_quant_job* jobs, int32_t n_jobs, int32_t n_heads,
+                                    void* stream) {
+  if (jobs == nullptr) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "jobs is NULL");
+  if (n_jobs < 1 || n_jobs > kMaxJobs)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "n_jobs = %d not in 1..3", n_jobs);
+  if (n_heads < 1) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "n_heads = %d < 1", n_heads);
+  QuantParams p{};
+  p.n_jobs = n_jobs;
+  uint64_t total = 0;
+  for (int j = 0; j < n_jobs; ++j) {
+    const mla_quant_job& s = jobs[j];
+    if (s.head_dim != 192 && s.head_dim != 128)
+      return mla::fail(MLA_ERR_UNSUPPORTED, "job %d: head_dim %d is not 192 or 128", j, s.head_dim);
+    if (s.n_tokens < 0) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "job %d: n_tokens < 0", j);
+    if (s.n_tokens > 0 && (s.x == nullptr || s.y == nullptr || s.descale == nullptr))
+      return mla::fail(MLA_ERR_INVALID_ARGUMENT, "job %d: NULL pointer", j);
+    if (s.stride_token < 0 || s.stride_head < 0)
+      return mla::fail(MLA_ERR_INVALID_ARGUMENT, "job %d: negative stride", j);
+    if (s.n_tokens > 0 && !mla::aligned16(s.y))
+      return mla::fail(MLA_ERR_INVALID_ARGUMENT, "job %d: y is not 16-byte aligned", j);
+    if ((reinterpret_cast<uintptr_t>(s.x) & 1u) != 0)
+      return mla::fail(MLA_ERR_INVALID_ARGUMENT, "job %d: x is not 2-byte aligned", j);
+    const uint64_t rows = static_cast<uint64_t>(s.n_tokens) * static_cast<uint64_t>(n_heads);
+    const uint64_t chunks = rows * static_cast<uint64_t>(s.head_dim / 16);
+    if (rows >= (1ull << 31))
+      return mla::fail(MLA_ERR_UNSUPPORTED, "job %d: n_tokens * n_heads >= 2^31", j);
+    QuantJobDev& d = p.job[j];
+    d.x = static_cast<const uint16_t*>(s.x);
+    d.y = static_cast<uint8_t*>(s.y);
+    d.descale = s.descale;
+    d.stride_token = s.stride_token;
+    d.stride_head = s.stride_head;
+    d.head_dim = s.head_dim;
+    d.chunk_begin = static_cast<uint32_t>(total);
+    d.n_chunks = static_cast<uint32_t>(chunks);
+    d.vec = (mla::aligned16(s.x) && (s.stride_token % 8) == 0 && (s.stride_head % 8) == 0) ? 1 : 0;
+    total += chunks;
+    if (total >= (1ull << 31))
+      return mla::fail(MLA_ERR_UNSUPPORTED, "more than 2^35 elements in one launch");
+  }
+  if (total == 0) return mla::ok();
+  p.total_chunks = static_cast<uint32_t>(total);
+  p.heads = mla::make_fastdiv(static_cast<uint32_t>(n_heads));
+  hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(total, kQuantThreads)),
+                     dim3(kQuantThreads), 0, static_cast<hipStream_t>(stream), p);
+  return mla::check_launch("quant_static_kernel");
+}
+
+extern "C" int mla_fp8_amax_per_head(const void* x, int64_t stride_token, int64_t stride_head,
+                                     int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                                     float* amax, void* stream) {
+  if (amax == nullptr) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "amax is NULL");
+  if (n_heads < 1) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "n_heads = %d < 1", n_heads);
+  if (head_dim != 192 && head_dim != 128)
+    return mla::fail(MLA_ERR_UNSUPPORTED, "head_dim %d is not 192 or 128", head_dim);
+  if (n_tokens < 0 || stride_token < 0 || stride_head < 0)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "negative size or stride");
+  if (n_tokens > 0 && x == nullptr) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "x is NULL");
+  if ((reinterpret_cast<uintptr_t>(x) & 1u) != 0)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "x is not 2-byte aligned");
+  const uint64_t rows = static_cast<uint64_t>(n_tokens) * static_cast<uint64_t>(n_heads);
+  if (rows >= (1ull << 31)) return mla::fail(MLA_ERR_UNSUPPORTED, "n_tokens * n_heads >= 2^31");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((n_heads + kQuantThreads - 1) / kQuantThreads),
+                     dim3(kQuantThreads), 0, st, bits, n_heads);
+  int s = mla::check_launch("zero_words_kernel");
+  if (s != MLA_OK || rows == 0) return s;
+  AmaxParams p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.stride_token = stride_token;
+  p.stride_head = stride_head;
+  p.amax_bits = bits;
+  p.n_rows = static_cast<uint32_t>(rows);
+  p.head_dim = head_dim;
+  p.heads = mla::make_fastdiv(static_cast<uint32_t>(n_heads));
+  uint64_t blocks = (rows + 63) / 64;  // ~16 rows per wave
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(amax_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads), 0, st,
+                     p);
+  return mla::check_launch("amax_kernel");
+}

@@ -1,0 +1,189 @@
+/*
+ * mla_fp8.h -- C ABI of libmla_fp8.so: FP8 MLA context prefill for gfx950 (MI355X).
+ *
+ * The operations follow the vLLM pull request "[ROCm][MLA] Add guarded gfx942
+ * FP8 context prefill" (#51551): a one-kernel static per-head FP8 quantizer
+ * (Summary; "What this PR does"), a packed variable-length attention kernel for
+ * 12 heads with D192 Q/K and D128 V that keeps the model's attention boundary
+ * (Background; "What this PR does"), and context processed in segments with Q
+ * quantized once and its per-head scale reused ("What this PR does"), whose
+ * partial results are combined by a log-sum-exp merge.
+ *
+ * Conventions for every entry point
+ *   - Plain C: no C++ types and no exceptions cross this boundary.
+ *   - Device pointers are borrowed for the duration of the asynchronous call.
+ *     The library allocates nothing, keeps no pointer, creates no stream and
+ *     never synchronizes; work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream).
+ *   - Every scalar argument and pointer is checked on the host before any HIP
+ *     call; a failed check returns a status and launches nothing. There is no
+ *     silent fallback: unsupported shapes return MLA_ERR_UNSUPPORTED so that the
+ *     caller can take its own BF16 path (the pull request keeps BF16 for
+ *     unsupported shapes). A launch failure returns MLA_ERR_HIP.
+ *   - mla_last_error() gives a thread-local text for the last failure.
+ *   - Empty work (zero tokens, zero sequences) returns MLA_OK and launches nothing.
+ *   - Values the host cannot see without a device-to-host copy (cu_seqlens
+ *     contents, descale values in device memory) are the caller's contract.
+ *     Kernels clamp every sequence range to [0, total), so malformed cu_seqlens
+ *     give wrong numbers, never an out-of-bounds access.
+ *   - FP8 is OCP E4M3FN (finite maximum 448, no infinities); bf16 is the
+ *     upper half of IEEE binary32.
+ */
+#ifndef MLA_FP8_H
+#define MLA_FP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_FP8_ABI_VERSION 1
+
+enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad descale, ... */
+  MLA_ERR_UNSUPPORTED = 2,      /* valid request this library does not implement  */
+  MLA_ERR_HIP = 3               /* the HIP runtime reported an error              */
+};
+
+/* Library ABI version (MLA_FP8_ABI_VERSION at build time). */
+int mla_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* mla_status_string(int status);
+
+/* Thread-local text describing the last failure in this thread ("" if none). */
+const char* mla_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Static per-head quantizer                                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One tensor for mla_fp8_quant_static.
+ *   x        device, bf16, logical [n_tokens, n_heads, head_dim]; element
+ *            (t, h, d) at x + t*stride_token + h*stride_head + d (strides in
+ *            elements; the last dimension is contiguous). Token and head
+ *            strides let non-contiguous views be quantized in place.
+ *   descale  device, fp32 [n_heads]; must be finite, positive, in
+ *            [2^-126, 2^126] (check with mla_check_descales_host).
+ *   y        device, E4M3 codes, contiguous [n_tokens, n_heads, head_dim].
+ *   head_dim 192 (Q, K) or 128 (V), else MLA_ERR_UNSUPPORTED.
+ */
+typedef struct mla_quant_job {
+  const void* x;
+  int64_t stride_token;
+  int64_t stride_head;
+  int64_t n_tokens;
+  int32_t head_dim;
+  const float* descale;
+  void* y;
+} mla_quant_job;
+
+/*
+ * Quantize 1..3 tensors (Q, K, V or K, V) in ONE kernel launch:
+ *   y[t,h,d] = E4M3(x[t,h,d] / descale[h])
+ * E4M3 is the correctly rounded value of the exact quotient: round to nearest,
+ * ties to even; |quotient| > 448 (and +-Inf) saturates to +-448; NaN gives
+ * 0x7F with the input's sign; the sign of zero and of underflow is kept.
+ * Follows "[ROCm][MLA] Add guarded gfx942 FP8 context prefill", Summary and
+ * "What this PR does" (one-kernel static quantizer, no runtime amax).
+ * Fast path: x 16-byte aligned and both strides multiples of 8 elements;
+ * other strides take a slower element-wise path. y must be 16-byte aligned.
+ */
+int mla_fp8_quant_static(const mla_quant_job* jobs, int32_t n_jobs, int32_t n_heads,
+                         void* stream);
+
+/*
+ * Calibration: amax[h] = max |x[t,h,d]| over all tokens and dims (device fp32
+ * [n_heads], overwritten). Bit-exact (max does not depend on order). The
+ * pull request collects per-head maxima in a calibration pass ("What this PR
+ * does"); this is that reduction for one tensor. Same x layout and
+ * alignment rules as mla_quant_job. n_tokens == 0 writes zeros.
+ */
+int mla_fp8_amax_per_head(const void* x, int64_t stride_token, int64_t stride_head,
+                          int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                          float* amax, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Varlen context-prefill attention                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * FP8 attention over packed variable-length sequences, returning out and LSE.
+ * Follows "[ROCm][MLA] Add guarded gfx942 FP8 context prefill", Background
+ * (packed variable-length D192/V128 kernel) and "What this PR does" (12 heads,
+ * D192 Q/K, D128 V, FP8 Q/K/V with per-head scales).
+ *
+ *   q, k, v       device E4M3 codes, contiguous [total_q, n_heads, 192],
+ *                 [total_k, n_heads, 192], [total_k, n_heads, 128]; 16-byte aligned
+ *   cu_seqlens_q  device int32 [batch + 1], sequence b has query tokens
+ *   cu_seqlens_k  [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key tokens
+ *                 [cu_seqlens_k[b], cu_seqlens_k[b+1]); non-decreasing, last = total
+ *   max_seqlen_q  >= every query length (sets the grid; longer rows are not computed)
+ *   descale_q/k/v device fp32 [n_heads]: dequantized value = code value * descale
+ *   softmax_scale finite, > 0; logits are softmax_scale * <q_i, k_j> (dequantized)
+ *   causal        0: every key visible; 1: key j visible to query i iff
+ *                 j <= i + (Lk - Lq) (bottom-right aligned; the plain lower
+ *                 triangle when Lq == Lk)
+ *   out           device bf16 [total_q, n_heads, 128], caller-allocated, 16-byte aligned:
+ *                 out_i = sum_j softmax_ij * v_j (dequantized)
+ *   lse           device fp32, NULL or [n_heads, lse_stride] (lse_stride >= total_q):
+ *                 lse[h*lse_stride + i] = ln sum_j exp(logit_ij)
+ *   A query row with no visible key gets out = 0 and lse = -inf.
+ *   head_dim_qk/head_dim_v other than 192/128 -> MLA_ERR_UNSUPPORTED.
+ *   Any n_heads >= 1 is accepted (heads are independent; the workloads use 12).
+ */
+int mla_fp8_prefill_varlen(const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           int64_t total_q, int64_t total_k, int32_t n_heads,
+                           int32_t head_dim_qk, int32_t head_dim_v,
+                           const float* descale_q, const float* descale_k,
+                           const float* descale_v, float softmax_scale, int32_t causal,
+                           void* out, float* lse, int64_t lse_stride, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* LSE merge across context segments                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Combine n_segments partial results over disjoint key sets:
+ *   L = ln sum_s exp(L_s),   out = sum_s exp(L_s - L) * out_s
+ * (segments with L_s = -inf get weight 0; all -inf gives out = 0, L = -inf).
+ * The pull request reuses one quantized Q across context segments and keeps a
+ * per-chunk output buffer ("What this PR does"); the merge rule is the
+ * log-sum-exp identity for softmax over a union of key sets.
+ *
+ *   outs        host array of n_segments device pointers, bf16 [total_q, n_heads, 128],
+ *               16-byte aligned
+ *   lses        host array of n_segments device pointers, fp32 [n_heads, lse_in_stride]
+ *   out         device bf16 [total_q, n_heads, 128]; may be exactly one of outs[s]
+ *   lse_out     device fp32 [n_heads, lse_out_stride] or NULL; may be exactly one of
+ *               lses[s] when lse_out_stride == lse_in_stride
+ *   1 <= n_segments <= 64; head_dim_v must be 128.
+ */
+int mla_merge_lse(int32_t n_segments, const void* const* outs, const float* const* lses,
+                  int64_t lse_in_stride, int64_t total_q, int32_t n_heads,
+                  int32_t head_dim_v, void* out, float* lse_out, int64_t lse_out_stride,
+                  void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host-only helpers (no device access; usable without a GPU)                */
+/* ------------------------------------------------------------------------ */
+
+/* MLA_OK if all n descales are finite, positive and in [2^-126, 2^126], else
+ * MLA_ERR_INVALID_ARGUMENT (the pull request validates finite positive descales
+ * before use: "What this PR does"). */
+int mla_check_descales_host(const float* descale, int32_t n);
+
+/* descale_out[i] = amax[i] / 448 in IEEE fp32 (correctly rounded); every amax
+ * must be finite and > 0, else MLA_ERR_INVALID_ARGUMENT and nothing is written. */
+int mla_descale_from_amax_host(const float* amax, int32_t n, float* descale_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_FP8_H */

@@ -1,0 +1,138 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol that
+include/mla_fp8.h declares, its host helpers match the oracle bit for bit,
+and argument validation returns the documented status before any HIP call
+(no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from fp8_mla_context_amd import binding
+from fp8_mla_context_amd.build import LIB_PATH, build
+from oracle import descale_from_amax
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        build()
+    return binding.lib()
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert "mla_fp8_prefill_varlen" in names and "mla_merge_lse" in names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in binding.SIGNATURES, n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mla_abi_version() == 1
+    assert binding.status_string(0) == "MLA_OK"
+    assert binding.status_string(2) == "MLA_ERR_UNSUPPORTED"
+    assert binding.status_string(99) == "MLA_ERR_UNKNOWN"
+
+
+def test_check_descales_host(lib):
+    binding.check_descales_host(np.array([1.0, 0.01, 2.0 ** -126, 2.0 ** 126], np.float32))
+    for bad in (0.0, -1.0, np.inf, np.nan, 2.0 ** -127, 2.0 ** 127):
+        with pytest.raises(binding.MlaError) as e:
+            binding.check_descales_host(np.array([1.0, bad], np.float32))
+        assert e.value.status == binding.MLA_ERR_INVALID_ARGUMENT
+        assert "descale[1]" in binding.last_error()
+
+
+def test_descale_from_amax_host_matches_oracle(lib):
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0x0600, 0x7F7F, size=20000).astype(np.uint32) << 16
+    amax = bits.view(np.float32)
+    assert np.array_equal(binding.descale_from_amax_host(amax), descale_from_amax(amax))
+    with pytest.raises(binding.MlaError):
+        binding.descale_from_amax_host(np.array([1.0, 0.0], np.float32))
+
+
+def _prefill(lib, **kw):
+    args = dict(q=1 << 12, k=1 << 12, v=1 << 12, cu_q=1 << 12, cu_k=1 << 12, batch=1,
+                max_q=128, max_k=128, total_q=128, total_k=128, heads=12, dqk=192, dv_=128,
+                dq=1 << 12, dk=1 << 12, dv=1 << 12, scale=0.07, causal=1, out=1 << 12, lse=None,
+                lse_stride=128, stream=None)
+    args.update(kw)
+    return lib.mla_fp8_prefill_varlen(*args.values())
+
+
+def test_prefill_validation_before_launch(lib):
+    assert _prefill(lib, dqk=128) == binding.MLA_ERR_UNSUPPORTED
+    assert _prefill(lib, dv_=192) == binding.MLA_ERR_UNSUPPORTED
+    assert _prefill(lib, heads=0) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill(lib, causal=2) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill(lib, scale=0.0) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill(lib, scale=float("inf")) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill(lib, scale=float("nan")) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill(lib, q=None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill(lib, out=None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill(lib, dq=None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill(lib, q=(1 << 12) + 8) == binding.MLA_ERR_INVALID_ARGUMENT  # misaligned
+    assert _prefill(lib, lse=1 << 12, lse_stride=64) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill(lib, total_q=-1) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill(lib, total_q=1 << 31) == binding.MLA_ERR_UNSUPPORTED
+    # empty work: success without touching any pointer or the GPU
+    assert _prefill(lib, total_q=0, q=None, out=None) == binding.MLA_OK
+    assert _prefill(lib, batch=0) == binding.MLA_OK
+    assert _prefill(lib, max_q=0) == binding.MLA_OK
+
+
+def test_quant_validation_before_launch(lib):
+    job = binding.QuantJob(1 << 12, 192 * 12, 192, 10, 192, 1 << 12, 1 << 12)
+    jobs = (binding.QuantJob * 3)(job, job, job)
+    assert lib.mla_fp8_quant_static(jobs, 0, 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_fp8_quant_static(jobs, 4, 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_fp8_quant_static(None, 1, 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_fp8_quant_static(jobs, 1, 0, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    bad = binding.QuantJob(1 << 12, 192 * 12, 192, 10, 64, 1 << 12, 1 << 12)
+    assert lib.mla_fp8_quant_static((binding.QuantJob * 1)(bad), 1, 12, None) == binding.MLA_ERR_UNSUPPORTED
+    bad = binding.QuantJob(1 << 12, 192 * 12, 192, 10, 192, None, 1 << 12)
+    assert lib.mla_fp8_quant_static((binding.QuantJob * 1)(bad), 1, 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    bad = binding.QuantJob(1 << 12, 192 * 12, 192, 10, 192, 1 << 12, (1 << 12) + 4)
+    assert lib.mla_fp8_quant_static((binding.QuantJob * 1)(bad), 1, 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    empty = binding.QuantJob(None, 0, 0, 0, 192, None, None)
+    assert lib.mla_fp8_quant_static((binding.QuantJob * 1)(empty), 1, 12, None) == binding.MLA_OK
+
+
+def test_merge_validation_before_launch(lib):
+    P = ctypes.c_void_p
+    outs = (P * 2)(1 << 12, 1 << 13)
+    lses = (P * 2)(1 << 12, 1 << 13)
+    f = lib.mla_merge_lse
+    assert f(0, outs, lses, 16, 16, 12, 128, 1 << 12, None, 16, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(65, outs, lses, 16, 16, 12, 128, 1 << 12, None, 16, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(2, outs, lses, 16, 16, 12, 192, 1 << 12, None, 16, None) == binding.MLA_ERR_UNSUPPORTED
+    assert f(2, outs, lses, 8, 16, 12, 128, 1 << 12, None, 16, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(2, outs, lses, 16, 16, 12, 128, None, None, 16, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(2, outs, lses, 16, 16, 12, 128, (1 << 12) + 2, None, 16, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    # in-place LSE with a different stride is rejected
+    assert f(2, outs, lses, 16, 16, 12, 128, 1 << 12, 1 << 12, 32, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(2, outs, lses, 16, 0, 12, 128, None, None, 16, None) == binding.MLA_OK
+
+
+def test_amax_validation_before_launch(lib):
+    f = lib.mla_fp8_amax_per_head
+    assert f(1 << 12, 2304, 192, 4, 12, 192, None, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(1 << 12, 2304, 192, 4, 12, 64, 1 << 12, None) == binding.MLA_ERR_UNSUPPORTED
+    assert f(1 << 12, 2304, 192, -1, 12, 192, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f((1 << 12) + 1, 2304, 192, 4, 12, 192, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT

@@ -1,0 +1,153 @@
+"""GPU parity of the FP8 varlen prefill against the fp64 oracle.
+
+Element-wise on small shapes that span several 128-row query tiles and
+64-key tiles with ragged tails (causal and non-causal, Lq != Lk both ways,
+empty sequences); the full small workloads; sampled rows of the 32K-token
+causal workload in the launch configuration the benchmark times; and GPU-side
+invariants (run-to-run bitwise determinism, permutation of packed sequences,
+exact power-of-two V scaling, V = ones).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_workload
+from synth.inputs import make_random
+from tests.gpu_helpers import (dev, gpu_descales, gpu_prefill, gpu_quant, host, oracle_attention,
+                               oracle_codes, oracle_descales)
+from tests.parity import (assert_attention_parity, attention_errors, bf16_bits_to_f64, logit_scale,
+                          sigma_v)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_codes(B, wl, codes, ds_np, causal=None):
+    dcodes = [dev(c) for c in codes]
+    dds = [dev(d) for d in ds_np]
+    out, lse = gpu_prefill(B, wl, dcodes, dds, causal)
+    return bf16_bits_to_f64(host(out)), host(lse).astype(np.float64)
+
+
+def _check(B, wl, causal=None, label=""):
+    ds = oracle_descales(wl)
+    codes = oracle_codes(wl, ds)
+    out, lse = _run_codes(B, wl, codes, ds, causal)
+    ref_o, ref_l = oracle_attention(wl, codes, ds, causal)
+    errs = attention_errors(out, ref_o, lse, ref_l, sigma_v(wl),
+                            logit_scale(codes[0], codes[1], ds[0], ds[1], wl.softmax_scale))
+    print(label, errs, flush=True)
+    assert_attention_parity(errs, label)
+    # rows without a visible key are exactly zero
+    empty = ~np.isfinite(ref_l)  # [H, T]
+    if empty.any():
+        assert np.all(out.transpose(1, 0, 2)[empty] == 0.0)
+    return errs
+
+
+CASES = [
+    ("ragged_causal", [1, 5, 127, 128, 129, 300, 64, 0], None, True),
+    ("ragged_noncausal", [1, 5, 127, 128, 129, 300, 64, 0], None, False),
+    ("lk_gt_lq_causal", [100, 37, 200, 256], [300, 37, 64, 700], True),
+    ("lk_gt_lq_noncausal", [100, 37, 200, 256], [300, 37, 64, 700], False),
+    ("single_long", [777], None, True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)), ids=[c[0] for c in CASES])
+def test_prefill_small_cases(gpu_lib, case):
+    name, lq, lk, causal = CASES[case]
+    wl = make_random(100 + case, lq, lk, causal=causal, outliers=True)
+    _check(gpu_lib, wl, label=name)
+
+
+def test_prefill_c1_full_pipeline(gpu_lib):
+    """Workload C1 end to end through the library: calibration, one-launch quant, prefill."""
+    B = gpu_lib
+    wl = make_workload("C1")
+    d_gpu = gpu_descales(B, wl)
+    d_ref = oracle_descales(wl)
+    assert all(np.array_equal(a, b) for a, b in zip(d_gpu, d_ref))
+    codes, dds = gpu_quant(B, wl, d_gpu)
+    ref_codes = oracle_codes(wl, d_ref)
+    assert all(np.array_equal(host(c), r) for c, r in zip(codes, ref_codes))
+    out, lse = gpu_prefill(B, wl, codes, dds)
+    ref_o, ref_l = oracle_attention(wl, ref_codes, d_ref)
+    errs = attention_errors(bf16_bits_to_f64(host(out)), ref_o, host(lse).astype(np.float64), ref_l,
+                            sigma_v(wl), logit_scale(ref_codes[0], ref_codes[1], d_ref[0], d_ref[1],
+                                                     wl.softmax_scale))
+    print("C1", errs, flush=True)
+    assert_attention_parity(errs, "C1")
+
+
+def test_prefill_c2_full(gpu_lib):
+    _check(gpu_lib, make_workload("C2"), label="C2")
+
+
+def test_prefill_c3_sampled_rows(gpu_lib):
+    """32K causal at full size, same launch as the benchmark; oracle on sampled rows."""
+    B = gpu_lib
+    wl = make_workload("C3")
+    ds = gpu_descales(B, wl)
+    codes, dds = gpu_quant(B, wl, ds)
+    out, lse = gpu_prefill(B, wl, codes, dds)
+    rng = np.random.default_rng(3)
+    L = wl.total_q
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 129, L - 129, L - 128, L - 1],
+                                     rng.integers(0, L, 54)]))
+    c_np = [host(c) for c in codes]
+    ref_o, ref_l = oracle.attention_rows(c_np[0], c_np[1], c_np[2], wl.cu_seqlens_q,
+                                         wl.cu_seqlens_k, ds[0], ds[1], ds[2], wl.softmax_scale,
+                                         True, rows)
+    got_o = bf16_bits_to_f64(host(out[rows]))
+    got_l = host(lse[:, rows]).astype(np.float64)
+    errs = attention_errors(got_o, ref_o, got_l, ref_l, sigma_v(wl),
+                            logit_scale(c_np[0], c_np[1], ds[0], ds[1], wl.softmax_scale))
+    print("C3 sampled", errs, flush=True)
+    assert_attention_parity(errs, "C3 sampled")
+    # the quantizer bytes at full size are bit-exact as well (sampled tokens)
+    d_ref = oracle_descales(wl)
+    assert all(np.array_equal(a, b) for a, b in zip(ds, d_ref))
+    toks = np.unique(np.concatenate([[0, L - 1], rng.integers(0, L, 2000)]))
+    for c, x, d in zip(c_np, (wl.q, wl.k, wl.v), d_ref):
+        assert np.array_equal(c[toks], oracle.quant_static(x[toks], d))
+
+
+def test_determinism_and_permutation(gpu_lib):
+    B = gpu_lib
+    lens = [300, 129, 64, 1000, 7]
+    wl = make_random(5, lens, causal=True)
+    ds = oracle_descales(wl)
+    codes = oracle_codes(wl, ds)
+    o1, l1 = _run_codes(B, wl, codes, ds)
+    o2, l2 = _run_codes(B, wl, codes, ds)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    perm = [3, 0, 4, 2, 1]
+    cu = wl.cu_seqlens_q
+    idx = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in perm])
+    wl_p = make_random(5, [lens[b] for b in perm], causal=True)
+    codes_p = [c[idx] for c in codes]
+    op, lp = _run_codes(B, wl_p, codes_p, ds)
+    assert np.array_equal(op, o1[idx]) and np.array_equal(lp, l1[:, idx])
+
+
+def test_power_of_two_v_scale_is_exact(gpu_lib):
+    B = gpu_lib
+    wl = make_random(9, [200, 77], causal=True)
+    ds = oracle_descales(wl)
+    codes = oracle_codes(wl, ds)
+    o1, l1 = _run_codes(B, wl, codes, ds)
+    ds2 = [ds[0], ds[1], (ds[2] * 2).astype(np.float32)]
+    o2, l2 = _run_codes(B, wl, codes, ds2)
+    assert np.array_equal(o2, 2 * o1) and np.array_equal(l1, l2)
+
+
+def test_v_ones(gpu_lib):
+    B = gpu_lib
+    wl = make_random(11, [150, 64, 9], [150, 100, 9], causal=True)
+    ds = oracle_descales(wl)
+    codes = oracle_codes(wl, ds)
+    codes[2] = np.full_like(codes[2], 0x38)
+    ds[2] = np.ones_like(ds[2])
+    out, lse = _run_codes(B, wl, codes, ds)
+    assert np.max(np.abs(out - 1.0)) <= 4e-3
