@@ -65,6 +65,11 @@ SIGNATURES = {
     "mla_merge_lse": (ctypes.c_int, [
         _c_i32, ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp), _c_i64, _c_i64, _c_i32, _c_i32, _c_vp,
         _c_vp, _c_i64, _c_vp]),
+    "mla_fp8_prefill_chunked": (ctypes.c_int, [
+        _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_i32,
+        _c_i32, _c_vp, _c_vp, _c_i64, _c_vp, ctypes.c_uint64, _c_vp]),
+    "mla_fp8_chunked_workspace_size": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                                      ctypes.POINTER(ctypes.c_uint64)]),
     "mla_check_descales_host": (ctypes.c_int, [_c_fp, _c_i32]),
     "mla_descale_from_amax_host": (ctypes.c_int, [_c_fp, _c_i32, _c_fp]),
 }
@@ -138,7 +143,8 @@ def amax_per_head(x, stream=None):
     """x: bf16 [T, H, D] (last dim contiguous). Returns fp32 [H] on x's device."""
     import torch
 
-    assert x.dtype == torch.bfloat16 and x.dim() == 3 and x.stride(2) == 1
+    if x.dtype != torch.bfloat16 or x.dim() != 3 or (x.numel() > 0 and x.stride(2) != 1):
+        raise ValueError("x must be bf16 [T, H, D] with a contiguous last dim")
     amax = torch.empty(x.shape[1], dtype=torch.float32, device=x.device)
     _check(lib().mla_fp8_amax_per_head(_ptr(x), x.stride(0), x.stride(1), x.shape[0], x.shape[1],
                                        x.shape[2], _ptr(amax), _stream(stream)),
@@ -157,12 +163,14 @@ def quant_static(xs: Sequence, descales: Sequence, outs: Optional[Sequence] = No
     jobs = (QuantJob * len(xs))()
     ys = []
     for i, (x, d) in enumerate(zip(xs, descales)):
-        if x.dtype != torch.bfloat16 or x.dim() != 3 or x.stride(2) != 1 or x.shape[1] != heads:
+        if x.dtype != torch.bfloat16 or x.dim() != 3 or x.shape[1] != heads or \
+                (x.numel() > 0 and x.stride(2) != 1):
             raise ValueError("x must be bf16 [T, H, D] with a contiguous last dim")
         if d.dtype != torch.float32 or d.shape != (heads,) or not d.is_contiguous():
             raise ValueError("descale must be contiguous fp32 [H]")
         y = outs[i] if outs is not None else torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-        if y.dtype != torch.uint8 or tuple(y.shape) != tuple(x.shape) or not y.is_contiguous():
+        if y.dtype != torch.uint8 or tuple(y.shape) != tuple(x.shape) or \
+                (y.numel() > 0 and not y.is_contiguous()):
             raise ValueError("output must be contiguous uint8 with x's shape")
         jobs[i] = QuantJob(_ptr(x), x.stride(0), x.stride(1), x.shape[0], x.shape[2], _ptr(d),
                            _ptr(y))
@@ -225,3 +233,36 @@ def merge_lse(outs: Sequence, lses: Sequence, out=None, lse_out=None, stream=Non
     _check(lib().mla_merge_lse(n, op, lp, ld_in, tq, heads, D_V, _ptr(out), _ptr(lse_out),
                                lse_out.stride(0), _stream(stream)), "mla_merge_lse")
     return out, lse_out
+
+
+def chunked_workspace_size(lq: int, lk: int, n_heads: int, seg_len: int, causal: bool = True) -> int:
+    n = ctypes.c_uint64(0)
+    _check(lib().mla_fp8_chunked_workspace_size(lq, lk, n_heads, seg_len, int(bool(causal)),
+                                                ctypes.byref(n)), "mla_fp8_chunked_workspace_size")
+    return int(n.value)
+
+
+def prefill_chunked(q8, k8, v8, descale_q, descale_k, descale_v, softmax_scale: float, seg_len: int,
+                    causal: bool = True, out=None, lse=None, workspace=None, stream=None):
+    """One sequence of Lq queries (the last Lq of Lk tokens) over context segments of seg_len
+    keys with one quantized Q; partials merged in the library. Returns (out, lse)."""
+    import torch
+
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8 or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError("q8/k8/v8 must be contiguous uint8 [T, H, D]")
+    lq, heads = q8.shape[0], q8.shape[1]
+    lk = k8.shape[0]
+    if out is None:
+        out = torch.empty((lq, heads, D_V), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((heads, lq), dtype=torch.float32, device=q8.device)
+    need = chunked_workspace_size(lq, lk, heads, seg_len, causal)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q8.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mla_fp8_prefill_chunked(
+        _ptr(q8), _ptr(k8), _ptr(v8), lq, lk, heads, _ptr(descale_q), _ptr(descale_k),
+        _ptr(descale_v), float(softmax_scale), int(seg_len), int(bool(causal)), _ptr(out), _ptr(lse),
+        lse.stride(0), _ptr(workspace), ws_bytes, _stream(stream)), "mla_fp8_prefill_chunked")
+    return out, lse

@@ -1,0 +1,177 @@
+// Chunked-context prefill driver: one sequence, context attended segment by
+// segment with one quantized Q, partials merged by log-sum-exp.
+//
+// "[ROCm][MLA] Add guarded gfx942 FP8 context prefill" (vLLM #51551), "What
+// this PR does": Q is quantized once per context pass and its per-head scale
+// is reused across context segments; each segment writes into a per-chunk
+// output buffer. The segmentation itself is not written on the pages; the
+// plan used here, for Lq queries that are the last Lq of Lk keys
+// (off = Lk - Lq, bottom-right causal alignment):
+//   * queries are processed in chunks of seg rows;
+//   * keys [0, off) are cached context in segments of seg keys, visible in full
+//     to every query (non-causal calls);
+//   * for query chunk [r0, r1), the sequence's own keys [off, off + r0) come in
+//     segments of seg keys seen in full, and [off + r0, off + r1) is the
+//     diagonal (a causal call with Lq = Lk = r1 - r0); later keys are invisible;
+//   * non-causal requests split every query chunk over all key segments.
+// The host walks the plan; every step runs in the prefill and merge kernels on
+// the caller's stream. Partials are kept in fp32 in a caller-provided
+// workspace, so the output is rounded to bf16 once, by the merge; a query
+// chunk with a single part is written straight into `out`.
+#include <vector>
+
+#include "mla_internal.h"
+
+namespace {
+
+constexpr int kMaxParts = 64;  // the merge kernel's segment limit
+constexpr int64_t kAlign = 256;
+
+struct Part {
+  int64_t k0, k1;
+  int32_t causal;
+};
+
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Parts of query chunk [r0, r1). Returns false if the plan is not defined.
+bool chunk_parts(int64_t lq, int64_t lk, int64_t seg, int32_t causal, int64_t r0, int64_t r1,
+                 std::vector<Part>& parts) {
+  parts.clear();
+  if (!causal) {
+    for (int64_t k0 = 0; k0 < lk; k0 += seg) parts.push_back({k0, std::min(lk, k0 + seg), 0});
+    if (parts.empty()) parts.push_back({0, 0, 0});  // no keys: zeros and -inf
+    return true;
+  }
+  const int64_t off = lk - lq;
+  if (off < 0) return false;
+  for (int64_t k0 = 0; k0 < off; k0 += seg) parts.push_back({k0, std::min(off, k0 + seg), 0});
+  for (int64_t c0 = 0; c0 < r0; c0 += seg)
+    parts.push_back({off + c0, off + std::min(r0, c0 + seg), 0});
+  parts.push_back({off + r0, off + r1, 1});
+  return true;
+}
+
+int64_t max_parts(int64_t lq, int64_t lk, int64_t seg, int32_t causal) {
+  if (!causal) return std::max<int64_t>(1, (lk + seg - 1) / seg);
+  const int64_t off = lk - lq;
+  // the last chunk has the most parts
+  const int64_t last_r0 = lq > 0 ? ((lq - 1) / seg) * seg : 0;
+  return (off + seg - 1) / seg + (last_r0 + seg - 1) / seg + 1;
+}
+
+}  // namespace
+
+extern "C" int mla_fp8_chunked_workspace_size(int64_t lq, int64_t lk, int32_t n_heads,
+                                              int32_t seg_len, int32_t causal, uint64_t* bytes) {
+  if (bytes == nullptr) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (lq < 0 || lk < 0 || n_heads < 1 || seg_len < 1 || (causal != 0 && causal != 1))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "bad size, head count, segment length or causal");
+  if (causal && lk < lq)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "causal chunked prefill needs Lk >= Lq");
+  const int64_t n = max_parts(lq, lk, seg_len, causal);
+  if (n > kMaxParts)
+    return mla::fail(MLA_ERR_UNSUPPORTED, "%lld parts per query chunk exceed %d",
+                     static_cast<long long>(n), kMaxParts);
+  const int64_t rows = std::min<int64_t>(seg_len, lq);
+  const int64_t out_part = align_up(rows * n_heads * 128 * 4);
+  const int64_t lse_part = align_up(rows * n_heads * 4);
+  *bytes = (n > 1) ? static_cast<uint64_t>(n * (out_part + lse_part)) : 0u;
+  return mla::ok();
+}
+
+extern "C" int mla_fp8_prefill_chunked(const void* q, const void* k, const void* v, int64_t lq,
+                                       int64_t lk, int32_t n_heads, const float* descale_q,
+                                       const float* descale_k, const float* descale_v,
+                                       float softmax_scale, int32_t seg_len, int32_t causal,
+                                       void* out, float* lse, int64_t lse_stride, void* workspace,
+                                       uint64_t workspace_bytes, void* stream) {
+  int st = mla::prefill_check_common(n_heads, 192, 128, softmax_scale, causal);
+  if (st != MLA_OK) return st;
+  uint64_t need = 0;
+  st = mla_fp8_chunked_workspace_size(lq, lk, n_heads, seg_len, causal, &need);
+  if (st != MLA_OK) return st;
+  if (lq >= (1ll << 31) || lk >= (1ll << 31))
+    return mla::fail(MLA_ERR_UNSUPPORTED, "Lq and Lk must be < 2^31");
+  if (lq == 0) return mla::ok();
+  if (q == nullptr || out == nullptr || descale_q == nullptr || descale_k == nullptr ||
+      descale_v == nullptr || (lk > 0 && (k == nullptr || v == nullptr)))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!mla::aligned16(q) || !mla::aligned16(k) || !mla::aligned16(v) || !mla::aligned16(out))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
+  if (lse != nullptr && lse_stride < lq)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "lse_stride < Lq");
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !mla::aligned16(workspace)))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT,
+                     "workspace must be 16-byte aligned and hold %llu bytes",
+                     static_cast<unsigned long long>(need));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t seg = seg_len;
+  const int64_t rows_max = std::min<int64_t>(seg, lq);
+  const int64_t out_part = align_up(rows_max * n_heads * 128 * 4);
+  const int64_t lse_part = align_up(rows_max * n_heads * 4);
+  const int64_t n_max = max_parts(lq, lk, seg, causal);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* lse_ws = ws + n_max * out_part;
+  const uint8_t* q8 = static_cast<const uint8_t*>(q);
+  const uint8_t* k8 = static_cast<const uint8_t*>(k);
+  const uint8_t* v8 = static_cast<const uint8_t*>(v);
+  uint8_t* out8 = static_cast<uint8_t*>(out);
+  const int64_t qrow = static_cast<int64_t>(n_heads) * 192;
+  const int64_t vrow = static_cast<int64_t>(n_heads) * 128;
+  const int64_t orow = static_cast<int64_t>(n_heads) * 128 * 2;
+
+  std::vector<Part> parts;
+  const void* outs[kMaxParts];
+  const float* lses[kMaxParts];
+  for (int64_t r0 = 0; r0 < lq; r0 += seg) {
+    const int64_t r1 = std::min(lq, r0 + seg);
+    const int64_t rows = r1 - r0;
+    if (!chunk_parts(lq, lk, seg, causal, r0, r1, parts))
+      return mla::fail(MLA_ERR_INVALID_ARGUMENT, "no chunk plan");
+    const int n = static_cast<int>(parts.size());
+    for (int i = 0; i < n; ++i) {
+      const Part& pt = parts[i];
+      void* o = (n == 1) ? static_cast<void*>(out8 + r0 * orow) : static_cast<void*>(ws + i * out_part);
+      float* l_;
+      int64_t lstride;
+      if (n == 1) {
+        l_ = lse ? lse + r0 : nullptr;
+        lstride = lse_stride;
+      } else {
+        l_ = reinterpret_cast<float*>(lse_ws + i * lse_part);
+        lstride = rows;
+      }
+      mla::PrefillArgs a{q8 + r0 * qrow,
+                         k8 + pt.k0 * qrow,
+                         v8 + pt.k0 * vrow,
+                         nullptr,
+                         nullptr,
+                         1,
+                         static_cast<int32_t>(rows),
+                         rows,
+                         pt.k1 - pt.k0,
+                         n_heads,
+                         descale_q,
+                         descale_k,
+                         descale_v,
+                         softmax_scale,
+                         pt.causal,
+                         o,
+                         n > 1 ? 1 : 0,
+                         l_,
+                         lstride};
+      st = mla::prefill_launch(a, s);
+      if (st != MLA_OK) return st;
+      outs[i] = o;
+      lses[i] = l_;
+    }
+    if (n > 1) {
+      st = mla::merge_launch(n, outs, 1, lses, rows, rows, n_heads, out8 + r0 * orow,
+                             lse ? lse + r0 : nullptr, lse_stride, s);
+      if (st != MLA_OK) return st;
+    }
+  }
+  return mla::ok();
+}

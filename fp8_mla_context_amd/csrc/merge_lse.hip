@@ -19,7 +19,7 @@ constexpr int kMergeThreads = 256;
 constexpr int kMaxSegments = 64;
 
 struct MergeParams {
-  const uint16_t* outs[kMaxSegments];
+  const void* outs[kMaxSegments];
   const float* lses[kMaxSegments];
   uint16_t* out;
   float* lse_out;
@@ -33,6 +33,22 @@ struct MergeParams {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// 8 consecutive partial values of segment s as fp32
+template <bool kF32>
+__device__ __forceinline__ void load8(const void* base, int64_t eo, float v[8]) {
+  if (kF32) {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + eo);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + eo + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + eo);
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  }
+}
+
+template <bool kF32>
 __global__ __launch_bounds__(kMergeThreads) void merge_lse_kernel(MergeParams p) {
   const uint64_t n_threads = static_cast<uint64_t>(p.n_rows) * 16u;
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kMergeThreads;
@@ -52,11 +68,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_lse_kernel(MergeParams p)
       for (int s = 0; s < p.n_seg; ++s) {
         const float w = __expf(p.lses[s][li] - m);  // exp(-inf) = 0 for empty segments
         tot += w;
-        const uint4 v = *reinterpret_cast<const uint4*>(p.outs[s] + eo);
-        acc[0] += w * bf16_lo(v.x); acc[1] += w * bf16_hi(v.x);
-        acc[2] += w * bf16_lo(v.y); acc[3] += w * bf16_hi(v.y);
-        acc[4] += w * bf16_lo(v.z); acc[5] += w * bf16_hi(v.z);
-        acc[6] += w * bf16_lo(v.w); acc[7] += w * bf16_hi(v.w);
+        float v[8];
+        load8<kF32>(p.outs[s], eo, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += w * v[i];
       }
     }
     const float inv = (m != -INFINITY) ? 1.0f / tot : 0.0f;
@@ -73,6 +88,39 @@ __global__ __launch_bounds__(kMergeThreads) void merge_lse_kernel(MergeParams p)
 }
 
 }  // namespace
+
+namespace mla {
+
+int merge_launch(int32_t n_segments, const void* const* outs, int32_t in_f32,
+                 const float* const* lses, int64_t lse_in_stride, int64_t total_q,
+                 int32_t n_heads, void* out, float* lse_out, int64_t lse_out_stride,
+                 hipStream_t stream) {
+  const uint64_t rows = static_cast<uint64_t>(total_q) * static_cast<uint64_t>(n_heads);
+  if (rows == 0) return ok();
+  MergeParams p{};
+  for (int s = 0; s < n_segments; ++s) {
+    p.outs[s] = outs[s];
+    p.lses[s] = lses[s];
+  }
+  p.out = static_cast<uint16_t*>(out);
+  p.lse_out = lse_out;
+  p.lse_in_stride = lse_in_stride;
+  p.lse_out_stride = lse_out_stride;
+  p.n_rows = static_cast<uint32_t>(rows);
+  p.n_seg = n_segments;
+  p.heads = make_fastdiv(static_cast<uint32_t>(n_heads));
+  uint64_t blocks = (rows * 16 + kMergeThreads - 1) / kMergeThreads;
+  if (blocks > 256ull * 16ull) blocks = 256ull * 16ull;
+  if (in_f32)
+    hipLaunchKernelGGL(merge_lse_kernel<true>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kMergeThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(merge_lse_kernel<false>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kMergeThreads), 0, stream, p);
+  return check_launch("merge_lse_kernel");
+}
+
+}  // namespace mla
 
 extern "C" int mla_merge_lse(int32_t n_segments, const void* const* outs, const float* const* lses,
                              int64_t lse_in_stride, int64_t total_q, int32_t n_heads,
@@ -95,25 +143,12 @@ extern "C" int mla_merge_lse(int32_t n_segments, const void* const* outs, const 
     return mla::fail(MLA_ERR_INVALID_ARGUMENT, "lse_out_stride < total_q");
   const uint64_t rows = static_cast<uint64_t>(total_q) * static_cast<uint64_t>(n_heads);
   if (rows >= (1ull << 31)) return mla::fail(MLA_ERR_UNSUPPORTED, "total_q * n_heads >= 2^31");
-  MergeParams p{};
   for (int s = 0; s < n_segments; ++s) {
     if (outs[s] == nullptr || lses[s] == nullptr || !mla::aligned16(outs[s]))
       return mla::fail(MLA_ERR_INVALID_ARGUMENT, "segment %d: NULL or misaligned pointer", s);
     if (lse_out != nullptr && lses[s] == lse_out && lse_out_stride != lse_in_stride)
       return mla::fail(MLA_ERR_INVALID_ARGUMENT, "in-place LSE merge needs equal strides");
-    p.outs[s] = static_cast<const uint16_t*>(outs[s]);
-    p.lses[s] = lses[s];
   }
-  p.out = static_cast<uint16_t*>(out);
-  p.lse_out = lse_out;
-  p.lse_in_stride = lse_in_stride;
-  p.lse_out_stride = lse_out_stride;
-  p.n_rows = static_cast<uint32_t>(rows);
-  p.n_seg = n_segments;
-  p.heads = mla::make_fastdiv(static_cast<uint32_t>(n_heads));
-  uint64_t blocks = (rows * 16 + kMergeThreads - 1) / kMergeThreads;
-  if (blocks > 256ull * 16ull) blocks = 256ull * 16ull;
-  hipLaunchKernelGGL(merge_lse_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kMergeThreads), 0,
-                     static_cast<hipStream_t>(stream), p);
-  return mla::check_launch("merge_lse_kernel");
+  return mla::merge_launch(n_segments, outs, 0, lses, lse_in_stride, total_q, n_heads, out,
+                           lse_out, lse_out_stride, static_cast<hipStream_t>(stream));
 }

@@ -48,4 +48,37 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   return (x != x) ? ((b >> 16) | 0x40u) : r;
 }
 
+// One prefill launch. cu_q/cu_k may be NULL: then batch must be 1 and the
+// sequence spans total_q queries and total_k keys. Head dims are 192/128.
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t batch;
+  int32_t max_seqlen_q;
+  int64_t total_q;
+  int64_t total_k;
+  int32_t n_heads;
+  const float* dq;
+  const float* dk;
+  const float* dv;
+  float softmax_scale;
+  int32_t causal;
+  void* out;        // bf16 [total_q, n_heads, 128], or fp32 when out_f32 = 1
+  int32_t out_f32;
+  float* lse;
+  int64_t lse_stride;
+};
+int prefill_launch(const PrefillArgs& a, hipStream_t stream);
+
+// LSE merge launch with validated arguments; partials are bf16 or (in_f32) fp32.
+int merge_launch(int32_t n_segments, const void* const* outs, int32_t in_f32,
+                 const float* const* lses, int64_t lse_in_stride, int64_t total_q,
+                 int32_t n_heads, void* out, float* lse_out, int64_t lse_out_stride,
+                 hipStream_t stream);
+int prefill_check_common(int32_t n_heads, int32_t head_dim_qk, int32_t head_dim_v,
+                         float softmax_scale, int32_t causal);
+
 }  // namespace mla

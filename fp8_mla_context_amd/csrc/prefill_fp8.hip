@@ -39,7 +39,8 @@
 //  * Causal (bottom-right aligned: key j visible to row i iff j <= i + Lk - Lq):
 //    a wave skips tiles past its last visible key; only tiles that cross the
 //    diagonal or the ragged end are masked element-wise.
-//  * Epilogue: out = O * dv / l in bf16, lse = ln2 * (m + log2 l - 8).
+//  * Epilogue: out = O * dv / l in bf16 (fp32 for the partials of a chunked
+//    pass), lse = ln2 * (m + log2 l - 8).
 #include "mla_internal.h"
 
 namespace {
@@ -73,7 +74,7 @@ struct PrefillParams {
   const float* dq;
   const float* dk;
   const float* dv;
-  uint16_t* out;
+  void* out;
   float* lse;
   int64_t lse_stride;
   int64_t total_q;
@@ -82,6 +83,7 @@ struct PrefillParams {
   int32_t n_heads;
   int32_t n_m_tiles;
   int32_t causal;
+  int32_t out_f32;  // 1: out is fp32 (partials of a chunked pass), 0: bf16
   float scale_log2;
 };
 
@@ -128,8 +130,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(PrefillParams 
   idx /= p.batch;
   const int m_tile = p.n_m_tiles - 1 - idx;
 
-  int64_t q0 = p.cu_q[b], q1 = p.cu_q[b + 1];
-  int64_t k0 = p.cu_k[b], k1 = p.cu_k[b + 1];
+  // packed sequences from cu_seqlens, or one sequence spanning all tokens
+  int64_t q0 = 0, q1 = p.total_q, k0 = 0, k1 = p.total_k;
+  if (p.cu_q != nullptr) {
+    q0 = p.cu_q[b];
+    q1 = p.cu_q[b + 1];
+    k0 = p.cu_k[b];
+    k1 = p.cu_k[b + 1];
+  }
   q0 = min(max(q0, (int64_t)0), p.total_q);
   q1 = min(max(q1, q0), p.total_q);
   k0 = min(max(k0, (int64_t)0), p.total_k);
@@ -306,18 +314,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(PrefillParams 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (row_ok) {
     const float inv = (l_tot > 0.f) ? p.dv[h] / l_tot : 0.f;
-    uint16_t* op = p.out + (q0 + my_row) * (static_cast<int64_t>(H) * kDv) + h * kDv;
+    const int64_t obase = (q0 + my_row) * (static_cast<int64_t>(H) * kDv) + h * kDv;
+    if (p.out_f32) {
+      float* op = static_cast<float*>(p.out) + obase;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int grp4 = 0; grp4 < 4; ++grp4) {
-        const uint32_t e0 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 0] * inv);
-        const uint32_t e1 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 1] * inv);
-        const uint32_t e2 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 2] * inv);
-        const uint32_t e3 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + 32 * db + 8 * grp4 + 4 * g) =
-            make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-      }
+        for (int grp4 = 0; grp4 < 4; ++grp4)
+          *reinterpret_cast<float4*>(op + 32 * db + 8 * grp4 + 4 * g) =
+              make_float4(o[db][4 * grp4 + 0] * inv, o[db][4 * grp4 + 1] * inv,
+                          o[db][4 * grp4 + 2] * inv, o[db][4 * grp4 + 3] * inv);
+    } else {
+      uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int grp4 = 0; grp4 < 4; ++grp4) {
+          const uint32_t e0 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 0] * inv);
+          const uint32_t e1 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 1] * inv);
+          const uint32_t e2 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 2] * inv);
+          const uint32_t e3 = mla::f32_to_bf16_rne(o[db][4 * grp4 + 3] * inv);
+          *reinterpret_cast<uint2*>(op + 32 * db + 8 * grp4 + 4 * g) =
+              make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+        }
+    }
     if (g == 0 && p.lse != nullptr)
       p.lse[static_cast<int64_t>(h) * p.lse_stride + q0 + my_row] =
           (l_tot > 0.f) ? (m_run + __log2f(l_tot) - 8.0f) * kLn2 : -INFINITY;
@@ -325,6 +345,53 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(PrefillParams 
 }
 
 }  // namespace
+
+namespace mla {
+
+int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
+  if (a.total_q == 0 || a.batch == 0 || a.max_seqlen_q == 0) return ok();
+  const int64_t n_m = (static_cast<int64_t>(a.max_seqlen_q) + kBM - 1) / kBM;
+  const int64_t blocks = n_m * a.batch * a.n_heads;
+  if (blocks >= (1ll << 31)) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
+  PrefillParams prm;
+  prm.q = static_cast<const uint8_t*>(a.q);
+  prm.k = static_cast<const uint8_t*>(a.k);
+  prm.v = static_cast<const uint8_t*>(a.v);
+  prm.cu_q = a.cu_q;
+  prm.cu_k = a.cu_k;
+  prm.dq = a.dq;
+  prm.dk = a.dk;
+  prm.dv = a.dv;
+  prm.out = a.out;
+  prm.out_f32 = a.out_f32;
+  prm.lse = a.lse;
+  prm.lse_stride = a.lse_stride;
+  prm.total_q = a.total_q;
+  prm.total_k = a.total_k;
+  prm.batch = a.batch;
+  prm.n_heads = a.n_heads;
+  prm.n_m_tiles = static_cast<int32_t>(n_m);
+  prm.causal = a.causal;
+  prm.scale_log2 = a.softmax_scale * 1.44269504088896340736f;
+  hipLaunchKernelGGL(prefill_fp8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     stream, prm);
+  return check_launch("prefill_fp8_kernel");
+}
+
+int prefill_check_common(int32_t n_heads, int32_t head_dim_qk, int32_t head_dim_v,
+                         float softmax_scale, int32_t causal) {
+  if (head_dim_qk != kDqk || head_dim_v != kDv)
+    return fail(MLA_ERR_UNSUPPORTED, "head dims %d/%d: only 192/128 are implemented", head_dim_qk,
+                head_dim_v);
+  if (n_heads < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "n_heads = %d < 1", n_heads);
+  if (causal != 0 && causal != 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "causal = %d is not 0 or 1", causal);
+  if (!(softmax_scale > 0.f) || !(softmax_scale <= 3.4028234663852886e38f))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and positive");
+  return MLA_OK;
+}
+
+}  // namespace mla
 
 extern "C" int mla_fp8_prefill_varlen(const void* q, const void* k, const void* v,
                                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -334,16 +401,10 @@ extern "C" int mla_fp8_prefill_varlen(const void* q, const void* k, const void* 
                                       const float* descale_q, const float* descale_k,
                                       const float* descale_v, float softmax_scale, int32_t causal,
                                       void* out, float* lse, int64_t lse_stride, void* stream) {
-  if (head_dim_qk != kDqk || head_dim_v != kDv)
-    return mla::fail(MLA_ERR_UNSUPPORTED, "head dims %d/%d: only 192/128 are implemented",
-                     head_dim_qk, head_dim_v);
+  int st = mla::prefill_check_common(n_heads, head_dim_qk, head_dim_v, softmax_scale, causal);
+  if (st != MLA_OK) return st;
   if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
     return mla::fail(MLA_ERR_INVALID_ARGUMENT, "negative size");
-  if (n_heads < 1) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "n_heads = %d < 1", n_heads);
-  if (causal != 0 && causal != 1)
-    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "causal = %d is not 0 or 1", causal);
-  if (!(softmax_scale > 0.f) || !(softmax_scale <= 3.4028234663852886e38f))
-    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and positive");
   if (total_q >= (1ll << 31) || total_k >= (1ll << 31))
     return mla::fail(MLA_ERR_UNSUPPORTED, "total_q and total_k must be < 2^31");
   if (total_q == 0 || batch == 0 || max_seqlen_q == 0) return mla::ok();
@@ -356,30 +417,8 @@ extern "C" int mla_fp8_prefill_varlen(const void* q, const void* k, const void* 
     return mla::fail(MLA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
   if (lse != nullptr && lse_stride < total_q)
     return mla::fail(MLA_ERR_INVALID_ARGUMENT, "lse_stride < total_q");
-  const int64_t n_m = (static_cast<int64_t>(max_seqlen_q) + kBM - 1) / kBM;
-  const int64_t blocks = n_m * batch * n_heads;
-  if (blocks >= (1ll << 31)) return mla::fail(MLA_ERR_UNSUPPORTED, "grid too large");
-
-  PrefillParams prm;
-  prm.q = static_cast<const uint8_t*>(q);
-  prm.k = static_cast<const uint8_t*>(k);
-  prm.v = static_cast<const uint8_t*>(v);
-  prm.cu_q = cu_seqlens_q;
-  prm.cu_k = cu_seqlens_k;
-  prm.dq = descale_q;
-  prm.dk = descale_k;
-  prm.dv = descale_v;
-  prm.out = static_cast<uint16_t*>(out);
-  prm.lse = lse;
-  prm.lse_stride = lse_stride;
-  prm.total_q = total_q;
-  prm.total_k = total_k;
-  prm.batch = batch;
-  prm.n_heads = n_heads;
-  prm.n_m_tiles = static_cast<int32_t>(n_m);
-  prm.causal = causal;
-  prm.scale_log2 = softmax_scale * 1.44269504088896340736f;
-  hipLaunchKernelGGL(prefill_fp8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), prm);
-  return mla::check_launch("prefill_fp8_kernel");
+  mla::PrefillArgs a{q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, total_q, total_k,
+                     n_heads, descale_q, descale_k, descale_v, softmax_scale, causal, out, 0, lse,
+                     lse_stride};
+  return mla::prefill_launch(a, static_cast<hipStream_t>(stream));
 }

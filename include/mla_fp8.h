@@ -170,6 +170,41 @@ int mla_merge_lse(int32_t n_segments, const void* const* outs, const float* cons
                   void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Chunked-context prefill (one sequence)                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Attention of Lq queries that are the last Lq of Lk tokens (bottom-right
+ * causal alignment; causal = 0: every key visible), computed over context
+ * segments of seg_len keys with ONE quantized Q, partials merged by
+ * mla_merge_lse. Follows "[ROCm][MLA] Add guarded gfx942 FP8 context prefill",
+ * "What this PR does" (Q quantized once per context pass, its per-head scale
+ * reused across context segments). The segmentation (not given on the pages):
+ * queries in chunks of seg_len rows; cached keys [0, Lk - Lq) in segments of
+ * seg_len, seen in full by every query; for query chunk [r0, r1) the own keys
+ * [Lk-Lq, Lk-Lq+r0) in segments of seg_len seen in full, then the diagonal
+ * [Lk-Lq+r0, Lk-Lq+r1) as a causal call. Partials stay in fp32 (workspace) and
+ * the merged output is rounded to bf16 once. The result equals
+ * mla_fp8_prefill_varlen on the whole sequence up to rounding.
+ *
+ *   q, k, v     device E4M3, contiguous [Lq, H, 192], [Lk, H, 192], [Lk, H, 128]
+ *   out, lse    as mla_fp8_prefill_varlen (lse may be NULL; lse_stride >= Lq)
+ *   workspace   device scratch of mla_fp8_chunked_workspace_size() bytes, 16-byte
+ *               aligned (may be NULL when that size is 0); contents are overwritten
+ *   causal = 1 requires Lk >= Lq. At most 64 segments per query chunk
+ *   (MLA_ERR_UNSUPPORTED beyond). Enqueues several launches on `stream`.
+ */
+int mla_fp8_prefill_chunked(const void* q, const void* k, const void* v, int64_t lq, int64_t lk,
+                            int32_t n_heads, const float* descale_q, const float* descale_k,
+                            const float* descale_v, float softmax_scale, int32_t seg_len,
+                            int32_t causal, void* out, float* lse, int64_t lse_stride,
+                            void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Workspace bytes that mla_fp8_prefill_chunked needs for these sizes (host only). */
+int mla_fp8_chunked_workspace_size(int64_t lq, int64_t lk, int32_t n_heads, int32_t seg_len,
+                                   int32_t causal, uint64_t* bytes);
+
+/* ------------------------------------------------------------------------ */
 /* Host-only helpers (no device access; usable without a GPU)                */
 /* ------------------------------------------------------------------------ */
 

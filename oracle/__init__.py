@@ -10,8 +10,8 @@ What it computes, and the passages it follows (all from the vLLM PR
 
   e4m3.py      OCP E4M3FN codec: decode table and saturating round-to-nearest-even
                encode (FP8 maximum = the dtype's finite maximum, as in the vLLM PR
-               "Fuse gated RMSNorm with per-token FP8 for KDA o_proj", #54254, review
-               thread on ``rmsnorm_gated_fp8_per_token``).
+               "[ROCm][Kimi-K3] Fuse gated RMSNorm with per-token FP8 for KDA o_proj",
+               #54254, review thread on ``rmsnorm_gated_fp8_per_token``).
   quant.py     static per-head quantization with caller-supplied descales (Summary;
                "What this PR does": one-kernel static quantizer, finite positive
                descales) and the calibration arithmetic descale = amax / 448.

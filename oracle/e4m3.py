@@ -1,9 +1,11 @@
 """OCP E4M3FN codec, exact, in float64.  (Oracle: test infrastructure only.)
 
 Format (OCP 8-bit floating point, E4M3 "fn" variant; named float8_e4m3fn on
-MI355X in the vLLM PR "FP8 o-projection for DeepSeek-V4.1-Flash MLA on MI355X",
-#57081; saturation bound = the dtype's finite maximum, 448, as in the vLLM PR
-"Fuse gated RMSNorm with per-token FP8 for KDA o_proj", #54254):
+MI355X in the vLLM PR "[ROCm][Perf] FP8 o-projection for DeepSeek-V4.1-Flash MLA
+on AMD MI355X", #57081, section Purpose; saturation bound = the dtype's finite
+maximum, 448, as in the vLLM PR "[ROCm][Kimi-K3] Fuse gated RMSNorm with
+per-token FP8 for KDA o_proj", #54254, review thread on
+rmsnorm_gated_fp8_per_token):
 
   code = s eeee mmm;  e = 0: (-1)^s * m * 2^-9 (subnormal)
                       e > 0: (-1)^s * (1 + m/8) * 2^(e-7)

@@ -34,6 +34,9 @@ def gpu_descales(B, wl):
     """Calibration through the library: device amax kernel, then host amax/448."""
     out = []
     for c in wl.calib():
+        if c.shape[0] == 0:
+            out.append(None)
+            continue
         amax = host(B.amax_per_head(dev_bf16(c)))
         d = B.descale_from_amax_host(amax)
         B.check_descales_host(d)

@@ -1,0 +1,146 @@
+"""Chunked-context prefill (one quantized Q over context segments, LSE merge).
+
+CPU: workspace sizing agrees with an independent count of the segment plan,
+and invalid requests fail before any HIP call.
+GPU: parity with the oracle's unsegmented attention on small ragged plans
+(element-wise), on the 4K-new-over-64K-cached workload at full size (sampled
+rows) and on the 128K-token workload processed in 16K segments (sampled rows).
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from fp8_mla_context_amd import binding
+from fp8_mla_context_amd.build import LIB_PATH, build
+from synth import make_workload
+from synth.inputs import make_random
+from tests.parity import (assert_attention_parity, attention_errors, bf16_bits_to_f64, logit_scale,
+                          sigma_v)
+
+
+@pytest.fixture(scope="module")
+def cpu_lib():
+    if not os.path.exists(LIB_PATH):
+        build()
+    return binding.lib()
+
+
+@pytest.mark.parametrize("lq,lk,seg,causal", [(4096, 69632, 16384, True), (131072, 131072, 16384, True),
+                                              (300, 1000, 128, True), (100, 700, 200, False),
+                                              (5, 5, 64, True), (64, 0, 32, False)])
+def test_workspace_size_matches_plan(cpu_lib, lq, lk, seg, causal):
+    plan = oracle.segment_plan(lq, max(lk, 1) if not causal and lk == 0 else lk, seg, causal)
+    n_max = max(1, max(len(p[2]) for p in plan))
+    rows = min(seg, lq)
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    exp = 0 if n_max == 1 else n_max * (al(rows * 12 * 512) + al(rows * 12 * 4))
+    assert binding.chunked_workspace_size(lq, lk, 12, seg, causal) == exp
+
+
+def test_chunked_validation(cpu_lib):
+    with pytest.raises(binding.MlaError) as e:
+        binding.chunked_workspace_size(100, 50, 12, 16, True)  # causal needs Lk >= Lq
+    assert e.value.status == binding.MLA_ERR_INVALID_ARGUMENT
+    with pytest.raises(binding.MlaError) as e:
+        binding.chunked_workspace_size(10, 10, 12, 0, True)
+    assert e.value.status == binding.MLA_ERR_INVALID_ARGUMENT
+    with pytest.raises(binding.MlaError) as e:
+        binding.chunked_workspace_size(1, 65 * 16 + 1, 12, 16, True)  # 66 parts
+    assert e.value.status == binding.MLA_ERR_UNSUPPORTED
+    f = cpu_lib.mla_fp8_prefill_chunked
+    args = [1 << 12, 1 << 12, 1 << 12, 100, 300, 12, 1 << 12, 1 << 12, 1 << 12, 0.07, 64, 1,
+            1 << 12, None, 100, None, 0, None]
+    assert f(*args) == binding.MLA_ERR_INVALID_ARGUMENT  # workspace missing
+    a = list(args)
+    a[9] = -1.0
+    assert f(*a) == binding.MLA_ERR_INVALID_ARGUMENT
+    a = list(args)
+    a[3] = 0
+    assert f(*a) == binding.MLA_OK  # no queries: nothing to do
+
+
+# ----------------------------------------------------------------------------- GPU
+
+def _gpu_codes(B, wl):
+    from tests.gpu_helpers import gpu_descales, gpu_quant
+
+    if wl.total_k == 0:  # nothing to calibrate K and V on: unit descales
+        ds = gpu_descales(B, wl)[:1] + [np.ones(wl.q.shape[1], np.float32)] * 2
+    else:
+        ds = gpu_descales(B, wl)
+    codes, dds = gpu_quant(B, wl, ds)  # one launch for Q, K and V
+    return ds, codes, dds
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("lq,lk,seg,causal", [(300, 1000, 128, True), (257, 257, 64, True),
+                                              (100, 700, 200, False), (130, 130, 1000, True),
+                                              (77, 0, 32, False)])
+def test_chunked_small_elementwise(gpu_lib, lq, lk, seg, causal):
+    from tests.gpu_helpers import host
+
+    B = gpu_lib
+    wl = make_random(lq * 7 + lk, [lq], [lk], causal=causal, outliers=True)
+    ds, codes, dds = _gpu_codes(B, wl)
+    out, lse = B.prefill_chunked(codes[0], codes[1], codes[2], dds[0], dds[1], dds[2],
+                                 wl.softmax_scale, seg, causal)
+    c_np = [host(c) for c in codes]
+    ref_o, ref_l = oracle.attention_varlen(*c_np, wl.cu_seqlens_q, wl.cu_seqlens_k, *ds,
+                                           wl.softmax_scale, causal)
+    errs = attention_errors(bf16_bits_to_f64(host(out)), ref_o, host(lse).astype(np.float64), ref_l,
+                            sigma_v(wl), logit_scale(c_np[0], c_np[1], ds[0], ds[1], wl.softmax_scale))
+    print((lq, lk, seg, causal), errs, flush=True)
+    assert_attention_parity(errs, f"chunked {(lq, lk, seg, causal)}")
+
+
+def _sampled_check(B, name, n_rows, label):
+    from tests.gpu_helpers import host
+
+    wl = make_workload(name)
+    ds, codes, dds = _gpu_codes(B, wl)
+    out, lse = B.prefill_chunked(codes[0], codes[1], codes[2], dds[0], dds[1], dds[2],
+                                 wl.softmax_scale, wl.segment_len, True)
+    lq = wl.total_q
+    rng = np.random.default_rng(wl.seed)
+    seg = wl.segment_len
+    edges = [0, lq - 1] + [r for r in range(0, lq, seg)] + [min(lq - 1, r + seg - 1) for r in range(0, lq, seg)]
+    rows = np.unique(np.concatenate([edges, rng.integers(0, lq, n_rows)]))
+    c_np = [host(c) for c in codes]
+    ref_o, ref_l = oracle.attention_rows(c_np[0], c_np[1], c_np[2], wl.cu_seqlens_q, wl.cu_seqlens_k,
+                                         ds[0], ds[1], ds[2], wl.softmax_scale, True, rows)
+    got_o = bf16_bits_to_f64(host(out[rows]))
+    got_l = host(lse[:, rows]).astype(np.float64)
+    errs = attention_errors(got_o, ref_o, got_l, ref_l, sigma_v(wl),
+                            logit_scale(c_np[0], c_np[1], ds[0], ds[1], wl.softmax_scale))
+    print(label, len(rows), "rows", errs, flush=True)
+    assert_attention_parity(errs, label)
+    return wl, codes, dds, out, lse
+
+
+@pytest.mark.gpu
+def test_c4_chunked_full_size(gpu_lib):
+    """4096 new queries over 65536 cached + 4096 new keys: 4 context segments + diagonal, merge of 5."""
+    B = gpu_lib
+    wl, codes, dds, out, lse = _sampled_check(B, "C4", 192, "C4 chunked")
+    # the chunked result and one unsegmented bottom-right causal call agree closely
+    import torch
+
+    cu_q = torch.tensor(wl.cu_seqlens_q, device="cuda")
+    cu_k = torch.tensor(wl.cu_seqlens_k, device="cuda")
+    o1, l1 = B.prefill_varlen(codes[0], codes[1], codes[2], cu_q, cu_k, wl.max_seqlen_q,
+                              wl.max_seqlen_k, dds[0], dds[1], dds[2], wl.softmax_scale, True)
+    a = bf16_bits_to_f64(o1.view(torch.int16).cpu().numpy().view(np.uint16))
+    b = bf16_bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    # each is within ~2.5e-3 rel-RMS of the oracle; their difference is of that order
+    assert np.sqrt(np.sum((a - b) ** 2) / np.sum(a ** 2)) < 6e-3
+    assert torch.max(torch.abs(l1 - lse)).item() < 1e-3
+
+
+@pytest.mark.gpu
+def test_c5_chunked_sampled(gpu_lib):
+    """131072 tokens in 8 segments of 16384: 36 prefill calls and 7 merges."""
+    _sampled_check(gpu_lib, "C5", 48, "C5 chunked")
