@@ -76,17 +76,19 @@ SIGNATURES = {
 
 
 def lib_path() -> str:
-    return LIB_PATH
+    """The in-tree library, or the file named by MLA_FP8_LIB (for comparing builds)."""
+    return os.environ.get("MLA_FP8_LIB", LIB_PATH)
 
 
 def lib() -> ctypes.CDLL:
     """Load the library once; raise if it has not been built."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(LIB_PATH):
+        path = lib_path()
+        if not os.path.exists(path):
             raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with `python -m fp8_mla_context_amd.build`")
-        handle = ctypes.CDLL(LIB_PATH)
+                f"{path} is missing: build it with `python -m fp8_mla_context_amd.build`")
+        handle = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)
             fn.restype = res

@@ -6,15 +6,17 @@
 // Q/K/V); the close comment separates causal and non-causal shapes.
 //
 // Design (gfx950, wave64):
-//  * One workgroup = 8 waves = 256 query rows of one (sequence, head); each
-//    wave owns 32 rows. Workgroups are ordered heaviest first: the flattened
+//  * One workgroup = 4 waves = 128 query rows of one (sequence, head); each
+//    wave owns 32 rows; two workgroups share a CU (two waves per SIMD from
+//    independent workgroups, so one's barrier stalls are covered by the other). Workgroups are ordered heaviest first: the flattened
 //    block index walks query tiles from the last (most keys under a causal
 //    mask) to the first, with heads and sequences fastest.
 //  * K/V tiles of 64 keys are staged in LDS in their natural [key][dim]
-//    layout, double-buffered: the global loads of tile t+1 are issued into
-//    registers before tile t is computed and stored to the other buffer after
-//    it, so one barrier per tile suffices and HBM/L2 latency hides behind the
-//    MFMA work.
+//    layout in three rotating buffers, filled by direct global->LDS loads (no
+//    register staging). The loop is software-pipelined: in iteration t a wave
+//    starts the loads of tile t+2, issues the S MFMAs of tile t+1, runs the
+//    softmax of tile t on the VALU while those execute, and issues the PV
+//    MFMAs of tile t as soon as each half of P is ready. One barrier per tile.
 //  * S^T = K * Q^T on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32): the
 //    Q fragment (32 rows x 192) stays in registers as the B operand, K rows
 //    are read from LDS as the A operand. In the 32x32 accumulator layout every
@@ -53,7 +55,11 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kDqk = 192;
 constexpr int kDv = 128;
-constexpr int kWaves = 8;
+#ifndef MLA_PREFILL_WAVES
+#define MLA_PREFILL_WAVES 4
+#endif
+constexpr int kWaves = MLA_PREFILL_WAVES;  // waves per workgroup
+constexpr int kWgPerCu = 8 / kWaves;       // resident workgroups per CU (2 waves per SIMD)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
@@ -64,6 +70,10 @@ constexpr int kVTile = kBN * kVStride;
 constexpr int kKChunks = kBN * kDqk / 16;  // 768 16-byte chunks per K tile
 constexpr int kVChunks = kBN * kDv / 16;   // 512 per V tile
 constexpr float kLn2 = 0.69314718055994530942f;
+// P' = 2^(logit*log2e - m + kPScaleLog2); the largest weight maps near 2^8, small
+// weights stay clear of E4M3 subnormals, and P' <= 2^(8 + kRescaleSlack) <= 448.
+constexpr float kPScaleLog2 = 8.0f;
+constexpr float kRescaleSlack = 0.75f;
 
 struct PrefillParams {
   const uint8_t* q;
@@ -103,19 +113,33 @@ __device__ __forceinline__ v2i read_tr8(const uint8_t* lds_ptr) {
       (__attribute__((address_space(3))) v2i*)(lds_ptr));
 }
 
-// Splits four weights into E4M3 hi/lo terms, packed 4 per dword.
-__device__ __forceinline__ void split_pack4(float p0, float p1, float p2, float p3, int& hw,
-                                            int& lw) {
-  hw = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-  hw = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, hw, true);
-  const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
-  const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-  lw = __builtin_amdgcn_cvt_pk_fp8_f32(p0 - h01.x, p1 - h01.y, 0, false);
-  lw = __builtin_amdgcn_cvt_pk_fp8_f32(p2 - h23.x, p3 - h23.y, lw, true);
+// P' with its mantissa truncated to 3 bits: exactly representable in E4M3 when P' >= 2^-6
+__device__ __forceinline__ float trunc_e4m3(float x) {
+  return __uint_as_float(__float_as_uint(x) & 0xFFF00000u);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (kKTile + kVTile)];
+// S^T block for one tile: two 32-key blocks, K-dim 192 = 3 x 64
+__device__ __forceinline__ void qk_tile(const uint8_t* kl, int col, int g, const v8i qf[3],
+                                        v16f s[2]) {
+#pragma unroll
+  for (int b2 = 0; b2 < 2; ++b2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[b2][r] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) {
+      const v8i a = load32(kl + (32 * b2 + col) * kKStride + 64 * kb + 32 * g);
+      s[b2] = mfma_f8(a, qf[kb], s[b2]);
+    }
+  }
+}
+
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+__global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(PrefillParams p) {
+  // three K/V tile buffers: tile t is in buffer t % 3
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * (kKTile + kVTile)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -150,15 +174,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(PrefillParams 
   const bool causal = p.causal != 0;
   int kend = Lk;
   if (causal) kend = min(Lk, max(0, min(Lq, row0 + kBM) + off));
+  const int n_tiles = (kend + kBN - 1) / kBN;
 
   const int g = lane >> 5;
   const int col = lane & 31;
   const int wrow0 = row0 + wave * 32;
   const int my_row = wrow0 + col;
   const bool row_ok = my_row < Lq;
-  const bool wave_active = wrow0 < Lq;
-  int wave_kend = kend;
-  if (causal) wave_kend = min(Lk, max(0, min(Lq, wrow0 + 32) + off));
+  // tiles this wave computes: [0, wave_tiles)
+  int wave_kend = (wrow0 < Lq) ? kend : 0;
+  if (causal && wrow0 < Lq) wave_kend = min(Lk, max(0, min(Lq, wrow0 + 32) + off));
+  const int wave_tiles = (wave_kend + kBN - 1) / kBN;
 
   const int64_t q_rs = static_cast<int64_t>(H) * kDqk;
   const int64_t k_rs = static_cast<int64_t>(H) * kDqk;
@@ -177,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(PrefillParams 
 
   const float c = p.dq[h] * p.dk[h] * p.scale_log2;
   float m_run = -INFINITY;
-  float l_run = 0.f;
+  float l_run = 0.f;  // this lane's part of the row sum (its 32 keys of every tile)
   v16f o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -187,29 +213,50 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(PrefillParams 
   const uint8_t* kbase = p.k + k0 * k_rs + h * kDqk;
   const uint8_t* vbase = p.v + k0 * v_rs + h * kDv;
 
-  // this thread's share of a tile load: K chunks tid and tid + 512 (< 768), V chunk tid
-  const int kr0 = tid / 12, kc0 = tid - 12 * (tid / 12);
-  const int kr1 = (tid + kThreads) / 12, kc1 = (tid + kThreads) - 12 * ((tid + kThreads) / 12);
-  const bool has_k1 = tid + kThreads < kKChunks;
-  const int vr = tid >> 3, vc = tid & 7;
-  v4i kreg0, kreg1, vreg;
-  auto load_tile = [&](int kt) {
-    const v4i z = v4i{0, 0, 0, 0};
-    kreg0 = (kt + kr0 < Lk) ? *reinterpret_cast<const v4i*>(kbase + (kt + kr0) * k_rs + kc0 * 16) : z;
-    kreg1 = (has_k1 && kt + kr1 < Lk)
-                ? *reinterpret_cast<const v4i*>(kbase + (kt + kr1) * k_rs + kc1 * 16)
-                : z;
-    vreg = (kt + vr < Lk) ? *reinterpret_cast<const v4i*>(vbase + (kt + vr) * v_rs + vc * 16) : z;
-  };
-  auto store_tile = [&](int buf) {
-    uint8_t* kl = lds + buf * (kKTile + kVTile);
-    uint8_t* vl = kl + kKTile;
-    *reinterpret_cast<v4i*>(kl + kr0 * kKStride + kc0 * 16) = kreg0;
-    if (has_k1) *reinterpret_cast<v4i*>(kl + kr1 * kKStride + kc1 * 16) = kreg1;
-    *reinterpret_cast<v4i*>(vl + vr * kVStride + vc * 16) = vreg;
+  // Tile fill by direct global->LDS loads (global_load_lds_dwordx4): one wave
+  // instruction writes 64 consecutive 16-byte LDS slots, lane l to slot l, from
+  // any per-lane global address. A K tile is 64 rows x 13 slots (12 data + 1 pad),
+  // a V tile 64 rows x 9 slots (8 data + 1 pad): 13 + 9 = 22 instructions per tile,
+  // dealt round-robin to the waves. Pad slots load a duplicate chunk; rows past the
+  // sequence load its last row (K logits there are masked to -inf and their P is 0,
+  // so the duplicate never contributes, and no uninitialised bytes are ever read).
+  constexpr int kKInstr = kBN * (kKStride / 16) / 64;  // 13
+  constexpr int kVInstr = kBN * (kVStride / 16) / 64;  // 9
+  constexpr int kInstr = kKInstr + kVInstr;
+  constexpr int kPer = (kInstr + kWaves - 1) / kWaves;
+  // per instruction slot: (row << 16) | chunk byte offset within the row
+  uint32_t dma_rc[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = wave + j * kWaves;
+    const int per_row = (i < kKInstr) ? 13 : 9;
+    const int slot = ((i < kKInstr) ? i : i - kKInstr) * 64 + lane;
+    const int row = slot / per_row;
+    const int chunk = min(slot - per_row * row, per_row - 2);  // pad slot -> last data chunk
+    dma_rc[j] = (static_cast<uint32_t>(row) << 16) | static_cast<uint32_t>(chunk * 16);
+  }
+  const uint32_t k_rs32 = static_cast<uint32_t>(k_rs), v_rs32 = static_cast<uint32_t>(v_rs);
+  auto kbuf = [&](int t) { return lds + (t % 3) * (kKTile + kVTile); };
+  // issue the loads of tile t into its buffer; they complete before the next barrier
+  auto issue_tile = [&](int t) {
+    uint8_t* buf = kbuf(t);
+    const int kt = t * kBN;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = wave + j * kWaves;  // wave-uniform
+      if (i < kInstr) {
+        const uint32_t row = static_cast<uint32_t>(min(kt + static_cast<int>(dma_rc[j] >> 16), Lk - 1));
+        const uint32_t col = dma_rc[j] & 0xFFFFu;
+        const bool is_k = i < kKInstr;
+        const uint8_t* src = is_k ? kbase + (row * k_rs32 + col) : vbase + (row * v_rs32 + col);
+        uint8_t* dst = buf + (is_k ? i * 1024 : kKTile + (i - kKInstr) * 1024);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      }
+    }
   };
 
-  // transposed-read addresses (see the header): lane -> (16-lane group G, source slot s)
+  // transposed-read addresses (see the header): lane -> (16-lane group, source slot)
   const int grp = lane >> 4, slot = lane & 15;
   const int tb = slot >> 1, tp = slot & 1;
   int vt_off[4];
@@ -219,99 +266,177 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(PrefillParams 
     vt_off[r] = key * kVStride + 16 * (grp & 1) + 8 * tp;
   }
 
-  if (kend > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  // prologue: tiles 0 and 1 in LDS, S of tile 0 computed
+  if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 1) issue_tile(1);
   __syncthreads();
+  v16f s_cur[2];
+  if (wave_tiles > 0) qk_tile(kbuf(0), col, g, qf, s_cur);
 
-  int it = 0;
-  for (int kt = 0; kt < kend; kt += kBN, ++it) {
-    const int cur = it & 1;
-    const bool has_next = kt + kBN < kend;
-    if (has_next) load_tile(kt + kBN);
+  // Softmax of one group of 4 keys (w = 0..7) of this lane's 32: P' = 2^(c*s + nbias);
+  // hi = P' truncated to 3 mantissa bits (exact in E4M3 for P' >= 2^-6; below that the
+  // conversion rounds it, an error under 2^-10), packed into phi[w]; lo = P' - hi kept
+  // in fp32 for the second term; the row sum accumulates the fp32 P'.
+  auto softmax_group = [&](const v16f(&sc)[2], float nbias, int w, v8i& phi, float(&lo)[32]) {
+    float pw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * w + j;
+      pw[j] = __builtin_amdgcn_exp2f(fmaf(sc[i >> 4][i & 15], c, nbias));
+    }
+    l_run += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+    const float h0 = trunc_e4m3(pw[0]), h1 = trunc_e4m3(pw[1]);
+    const float h2 = trunc_e4m3(pw[2]), h3 = trunc_e4m3(pw[3]);
+    const int hw = __builtin_amdgcn_cvt_pk_fp8_f32(h0, h1, 0, false);
+    phi[w] = __builtin_amdgcn_cvt_pk_fp8_f32(h2, h3, hw, true);
+    lo[4 * w + 0] = pw[0] - h0;
+    lo[4 * w + 1] = pw[1] - h1;
+    lo[4 * w + 2] = pw[2] - h2;
+    lo[4 * w + 3] = pw[3] - h3;
+  };
+  auto lo_group = [&](const float(&lo)[32], int w, v8i& plo) {
+    const int lw = __builtin_amdgcn_cvt_pk_fp8_f32(lo[4 * w + 0], lo[4 * w + 1], 0, false);
+    plo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(lo[4 * w + 2], lo[4 * w + 3], lw, true);
+  };
+  auto vt_operand = [&](const uint8_t* vl, int db) {
+    const uint8_t* vp = vl + 32 * db;
+    const v2i r0 = read_tr8(vp + vt_off[0]);
+    const v2i r1 = read_tr8(vp + vt_off[1]);
+    const v2i r2 = read_tr8(vp + vt_off[2]);
+    const v2i r3 = read_tr8(vp + vt_off[3]);
+    return v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+  };
+  // K operand of S MFMA k (k = 0..5 alternates the two 32-key blocks: consecutive MFMAs
+  // write different accumulators)
+  auto k_operand = [&](const uint8_t* kl, int k) {
+    const int b2 = k & 1, kb = k >> 1;
+    return load32(kl + (32 * b2 + col) * kKStride + 64 * kb + 32 * g);
+  };
+  // PV of one tile: each hi MFMA is followed by a quarter of the lo conversion, then the
+  // lo MFMAs (V^T read again rather than kept in registers).
+  auto pv_tile = [&](const uint8_t* vl, const v8i& phi, const float(&lo)[32]) {
+    v8i plo;
+    v8i va = vt_operand(vl, 0);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      v8i vn;
+      if (db < 3) vn = vt_operand(vl, db + 1);
+      o[db] = mfma_f8(va, phi, o[db]);
+      __builtin_amdgcn_sched_barrier(0);
+      lo_group(lo, 2 * db, plo);
+      lo_group(lo, 2 * db + 1, plo);
+      __builtin_amdgcn_sched_barrier(0);
+      if (db < 3) va = vn;
+    }
+    asm volatile("" ::: "memory");  // re-read V^T below instead of keeping it live
+    va = vt_operand(vl, 0);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      v8i vn;
+      if (db < 3) vn = vt_operand(vl, db + 1);
+      o[db] = mfma_f8(va, plo, o[db]);
+      if (db < 3) va = vn;
+    }
+  };
 
-    if (wave_active && kt < wave_kend) {
-      const uint8_t* kl = lds + cur * (kKTile + kVTile);
-      const uint8_t* vl = kl + kKTile;
-      // S^T tile: two 32-key blocks, K-dim 192 = 3 x 64
-      v16f s[2];
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[b2][r] = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 3; ++kb) {
-          const v8i a = load32(kl + (32 * b2 + col) * kKStride + 64 * kb + 32 * g);
-          s[b2] = mfma_f8(a, qf[kb], s[b2]);
-        }
-      }
+  // one pipelined iteration: S of tile it is in s_cur; S of tile it + 1 goes to s_next
+  auto step = [&](int it, v16f(&s_cur)[2], v16f(&s_next)[2]) {
+    // buffer (it + 2) % 3 held tile it - 1, which every wave finished before the last barrier
+    if (it + 2 < n_tiles) issue_tile(it + 2);
+    const bool cur = it < wave_tiles;
+    const bool nxt = it + 1 < wave_tiles;
 
+    float nbias = 0.f;
+    if (cur) {
+      const int kt = it * kBN;
       const bool need_mask = (kt + kBN > Lk) || (causal && kt + kBN - 1 > wrow0 + off);
       if (need_mask) {
+        // side-effect barrier: keeps this rare block a real branch (the compiler would
+        // otherwise if-convert it into selects executed on every tile)
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kt + 32 * b2 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= Lk || (causal && key > my_row + off)) s[b2][r] = -INFINITY;
+            if (key >= Lk || (causal && key > my_row + off)) s_cur[b2][r] = -INFINITY;
           }
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
-        mx = fmaxf(mx, fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1])));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c);  // c > 0; -inf stays -inf
-      if (__any(m_new > m_run)) {
+        mx = vmax3(mx, vmax3(s_cur[0][r], s_cur[0][r + 1], s_cur[1][r]), s_cur[1][r + 1]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float m_tile = mx * c;  // c > 0; -inf stays -inf
+      // Lazy rescale: keep the reference max m_run unless some row's max exceeds it
+      // by more than kRescaleSlack; then P' <= 2^(8 + slack) < 448 stays in E4M3.
+      if (__any(m_tile > m_run + kRescaleSlack)) {
+        asm volatile("" ::: "memory");  // keep the rescale a real branch (see above)
+        const float m_new = fmaxf(m_run, m_tile);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while m_run is -inf
-        l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        l_run *= alpha;
         m_run = m_new;
       }
-      const float nbias = 8.0f - ((m_run == -INFINITY) ? 0.f : m_run);
-
-      float lsum = 0.f;
-      v8i phi, plo;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int b2 = w >> 2;
-        const int r0 = 4 * (w & 3);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b2][r0 + 0], c, nbias));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b2][r0 + 1], c, nbias));
-        const float p2 = __builtin_amdgcn_exp2f(fmaf(s[b2][r0 + 2], c, nbias));
-        const float p3 = __builtin_amdgcn_exp2f(fmaf(s[b2][r0 + 3], c, nbias));
-        lsum += (p0 + p1) + (p2 + p3);
-        int hw, lw;
-        split_pack4(p0, p1, p2, p3, hw, lw);
-        phi[w] = hw;
-        plo[w] = lw;
-      }
-      l_run += lsum;
-
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint8_t* vp = vl + 32 * db;
-        const v2i r0 = read_tr8(vp + vt_off[0]);
-        const v2i r1 = read_tr8(vp + vt_off[1]);
-        const v2i r2 = read_tr8(vp + vt_off[2]);
-        const v2i r3 = read_tr8(vp + vt_off[3]);
-        const v8i a = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
-        o[db] = mfma_f8(a, phi, o[db]);
-        o[db] = mfma_f8(a, plo, o[db]);
-      }
+      nbias = kPScaleLog2 - ((m_run == -INFINITY) ? 0.f : m_run);
     }
 
-    if (has_next) store_tile(cur ^ 1);
+    if (cur && nxt) {
+      // the S MFMAs of the next tile, each followed by one or two softmax groups of this
+      // tile; the K operand of MFMA k+1 is read while MFMA k runs
+      const uint8_t* kl = kbuf(it + 1);
+      v8i phi;
+      float lo[32];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_next[b2][r] = 0.f;
+      v8i ka = k_operand(kl, 0);
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        v8i kn;
+        if (k < 5) kn = k_operand(kl, k + 1);
+        s_next[k & 1] = mfma_f8(ka, qf[k >> 1], s_next[k & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        softmax_group(s_cur, nbias, k, phi, lo);                  // groups 0..5
+        if (k >= 4) softmax_group(s_cur, nbias, k + 2, phi, lo);  // groups 6, 7
+        __builtin_amdgcn_sched_barrier(0);
+        if (k < 5) ka = kn;
+      }
+      pv_tile(kbuf(it) + kKTile, phi, lo);
+    } else if (cur) {
+      v8i phi;
+      float lo[32];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) softmax_group(s_cur, nbias, w, phi, lo);
+      pv_tile(kbuf(it) + kKTile, phi, lo);
+    } else if (nxt) {
+      qk_tile(kbuf(it + 1), col, g, qf, s_next);
+    }
     __syncthreads();
+  };
+
+  v16f s_alt[2];
+  for (int it = 0; it < n_tiles; it += 2) {
+    step(it, s_cur, s_alt);
+    if (it + 1 < n_tiles) step(it + 1, s_alt, s_cur);
   }
 
   // epilogue: this lane holds row my_row, dims 32*db + 8*(r/4) + 4*g + r%4
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  float l_tot;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
+                                                     false, false);
+    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   if (row_ok) {
     const float inv = (l_tot > 0.f) ? p.dv[h] / l_tot : 0.f;
     const int64_t obase = (q0 + my_row) * (static_cast<int64_t>(H) * kDv) + h * kDv;
@@ -340,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(PrefillParams 
     }
     if (g == 0 && p.lse != nullptr)
       p.lse[static_cast<int64_t>(h) * p.lse_stride + q0 + my_row] =
-          (l_tot > 0.f) ? (m_run + __log2f(l_tot) - 8.0f) * kLn2 : -INFINITY;
+          (l_tot > 0.f) ? (m_run + __log2f(l_tot) - kPScaleLog2) * kLn2 : -INFINITY;
   }
 }
 
@@ -350,6 +475,8 @@ namespace mla {
 
 int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   if (a.total_q == 0 || a.batch == 0 || a.max_seqlen_q == 0) return ok();
+  if (a.total_k * static_cast<int64_t>(a.n_heads) * kDqk >= (1ll << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "total_k * n_heads * 192 must be < 2^31");
   const int64_t n_m = (static_cast<int64_t>(a.max_seqlen_q) + kBM - 1) / kBM;
   const int64_t blocks = n_m * a.batch * a.n_heads;
   if (blocks >= (1ll << 31)) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
