@@ -52,6 +52,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kDqk = 192;
 constexpr int kDv = 128;
@@ -64,16 +65,16 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr int kKStride = 208;     // LDS bytes per K row: 192 + 16 (8 consecutive rows hit distinct banks)
-constexpr int kVStride = 144;     // LDS bytes per V row: 128 + 16
+constexpr int kVStride = 128;     // LDS bytes per V row, 16-byte chunks XOR-swizzled by key
 constexpr int kKTile = kBN * kKStride;
 constexpr int kVTile = kBN * kVStride;
 constexpr int kKChunks = kBN * kDqk / 16;  // 768 16-byte chunks per K tile
-constexpr int kVChunks = kBN * kDv / 16;   // 512 per V tile
 constexpr float kLn2 = 0.69314718055994530942f;
-// P' = 2^(logit*log2e - m + kPScaleLog2); the largest weight maps near 2^8, small
-// weights stay clear of E4M3 subnormals, and P' <= 2^(8 + kRescaleSlack) <= 448.
-constexpr float kPScaleLog2 = 8.0f;
+// P = 2^(logit*log2e - m) <= 2^kRescaleSlack; its E4M3 codes stand for 256 * P, so the
+// largest weight maps near 2^8, small weights stay clear of E4M3 subnormals, and
+// 256 * P <= 2^8.75 < 448.
 constexpr float kRescaleSlack = 0.75f;
+constexpr half2_t kOnes2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 
 struct PrefillParams {
   const uint8_t* q;
@@ -113,11 +114,6 @@ __device__ __forceinline__ v2i read_tr8(const uint8_t* lds_ptr) {
       (__attribute__((address_space(3))) v2i*)(lds_ptr));
 }
 
-// P' with its mantissa truncated to 3 bits: exactly representable in E4M3 when P' >= 2^-6
-__device__ __forceinline__ float trunc_e4m3(float x) {
-  return __uint_as_float(__float_as_uint(x) & 0xFFF00000u);
-}
-
 // S^T block for one tile: two 32-key blocks, K-dim 192 = 3 x 64
 __device__ __forceinline__ void qk_tile(const uint8_t* kl, int col, int g, const v8i qf[3],
                                         v16f s[2]) {
@@ -133,6 +129,66 @@ __device__ __forceinline__ void qk_tile(const uint8_t* kl, int col, int g, const
   }
 }
 
+// V tiles are stored with unpadded 128-byte rows; the 16-byte chunk c of key row k sits at
+// position c ^ v_swizzle(k). For the transposed reads (8 keys x two 16-byte halves of a
+// 32-dim block per 16 lanes) this spreads every group of 16 or 32 lanes over distinct
+// banks, with 32 or with 64 four-byte banks.
+__device__ __forceinline__ int v_swizzle(int key) { return (key & 3) | (((key >> 3) & 1) << 2); }
+
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
+}
+
+// global_load_lds_dwordx4 from base + off (base wave-uniform, off per lane) to LDS
+// address lds_addr + 16 * lane. Issued as inline assembly so that the compiler does not
+// wait for it before unrelated LDS reads; completion is tracked with wait_vmcnt.
+__device__ __forceinline__ void dma_load16(const uint8_t* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+// wait until at most n (wave-uniform, 0..15) vector-memory loads of this wave are outstanding
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+    case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+  }
+}
+
+// workgroup barrier without the blanket memory wait of __syncthreads (every LDS read
+// before it has been consumed by an MFMA, so it has completed)
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// a pointer that is the same in every lane, kept in scalar registers
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 __device__ __forceinline__ float vmax3(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
@@ -143,7 +199,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int H = p.n_heads;
 
   // heaviest query tiles first; heads, then sequences, vary fastest
@@ -185,6 +241,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   int wave_kend = (wrow0 < Lq) ? kend : 0;
   if (causal && wrow0 < Lq) wave_kend = min(Lk, max(0, min(Lq, wrow0 + 32) + off));
   const int wave_tiles = (wave_kend + kBN - 1) / kBN;
+  const int wave_iters = wave_tiles > 0 ? wave_tiles + 1 : 0;  // + the trailing PV
 
   const int64_t q_rs = static_cast<int64_t>(H) * kDqk;
   const int64_t k_rs = static_cast<int64_t>(H) * kDqk;
@@ -210,48 +267,74 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-  const uint8_t* kbase = p.k + k0 * k_rs + h * kDqk;
-  const uint8_t* vbase = p.v + k0 * v_rs + h * kDv;
+  const uint8_t* kbase = uniform_ptr(p.k + k0 * k_rs + h * kDqk);
+  const uint8_t* vbase = uniform_ptr(p.v + k0 * v_rs + h * kDv);
 
   // Tile fill by direct global->LDS loads (global_load_lds_dwordx4): one wave
-  // instruction writes 64 consecutive 16-byte LDS slots, lane l to slot l, from
-  // any per-lane global address. A K tile is 64 rows x 13 slots (12 data + 1 pad),
-  // a V tile 64 rows x 9 slots (8 data + 1 pad): 13 + 9 = 22 instructions per tile,
+  // instruction writes 64 consecutive 16-byte LDS slots, lane l to slot l, from any
+  // per-lane global address. A K tile is 64 rows x 13 slots (12 data + 1 pad), a V tile
+  // 64 rows x 9 slots (8 data + 1 pad); the 13 K and the 9 V instructions of a tile are
   // dealt round-robin to the waves. Pad slots load a duplicate chunk; rows past the
-  // sequence load its last row (K logits there are masked to -inf and their P is 0,
-  // so the duplicate never contributes, and no uninitialised bytes are ever read).
+  // sequence load its last row (K logits there are masked to -inf and their P is 0, so
+  // the duplicate never contributes, and no uninitialised bytes are ever read).
+  //
+  // Schedule: tile t lives in buffer t % 3. Iteration t reads K(t+1) (S of the next
+  // tile) and V(t-1) (PV of the previous tile) and issues K(t+3) and V(t+1), into the
+  // buffers that K(t) and V(t-2) left at the previous barrier. Everything iteration t+1
+  // reads (K(t+2), V(t)) was issued one iteration earlier, so the wait before the
+  // barrier lets this iteration's loads stay in flight: each wave waits until at most
+  // the number of loads it issued this iteration is outstanding (loads complete in order).
   constexpr int kKInstr = kBN * (kKStride / 16) / 64;  // 13
-  constexpr int kVInstr = kBN * (kVStride / 16) / 64;  // 9
-  constexpr int kInstr = kKInstr + kVInstr;
-  constexpr int kPer = (kInstr + kWaves - 1) / kWaves;
-  // per instruction slot: (row << 16) | chunk byte offset within the row
-  uint32_t dma_rc[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = wave + j * kWaves;
-    const int per_row = (i < kKInstr) ? 13 : 9;
-    const int slot = ((i < kKInstr) ? i : i - kKInstr) * 64 + lane;
-    const int row = slot / per_row;
-    const int chunk = min(slot - per_row * row, per_row - 2);  // pad slot -> last data chunk
-    dma_rc[j] = (static_cast<uint32_t>(row) << 16) | static_cast<uint32_t>(chunk * 16);
-  }
+  constexpr int kVInstr = kBN * (kVStride / 16) / 64;  // 8
+  constexpr int kPerK = (kKInstr + kWaves - 1) / kWaves;
+  constexpr int kPerV = (kVInstr + kWaves - 1) / kWaves;
+  const int n_k_instr = (kKInstr - wave + kWaves - 1) / kWaves;  // K loads of this wave per tile
+  const int n_v_instr = (kVInstr - wave + kWaves - 1) / kWaves;  // V loads
+  // Slot j of a K (V) tile (instruction i = wave + j * kWaves): this lane's tile row and
+  // the byte offset of its chunk within the row. Full tiles use a wave-uniform base plus
+  // row * row_stride + chunk (< 2^31, checked on the host); the ragged last tile clamps rows.
+  auto dma_row = [&](int j, bool is_k) {
+    const int slot = (wave + j * kWaves) * 64 + lane;
+    if (is_k) {
+      const int row = slot / 13;
+      const int chunk = min(slot - 13 * row, 11);  // pad slot -> last data chunk
+      return make_int2(row, 16 * chunk);
+    }
+    const int row = slot >> 3;  // V: LDS position slot & 7 holds chunk position ^ swizzle
+    return make_int2(row, 16 * ((slot & 7) ^ v_swizzle(row)));
+  };
   const uint32_t k_rs32 = static_cast<uint32_t>(k_rs), v_rs32 = static_cast<uint32_t>(v_rs);
-  auto kbuf = [&](int t) { return lds + (t % 3) * (kKTile + kVTile); };
-  // issue the loads of tile t into its buffer; they complete before the next barrier
-  auto issue_tile = [&](int t) {
-    uint8_t* buf = kbuf(t);
-    const int kt = t * kBN;
+  uint32_t dma_off_k[kPerK], dma_off_v[kPerV];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+  for (int j = 0; j < kPerK; ++j) {
+    const int2 rc = dma_row(j, true);
+    dma_off_k[j] = static_cast<uint32_t>(rc.x) * k_rs32 + static_cast<uint32_t>(rc.y);
+  }
+#pragma unroll
+  for (int j = 0; j < kPerV; ++j) {
+    const int2 rc = dma_row(j, false);
+    dma_off_v[j] = static_cast<uint32_t>(rc.x) * v_rs32 + static_cast<uint32_t>(rc.y);
+  }
+  auto kbuf = [&](int t) { return lds + (t % 3) * (kKTile + kVTile); };
+  // issue this wave's loads of the K (is_k) or V part of tile t
+  auto issue = [&](int t, bool is_k) {
+    const int kt = t * kBN;
+    const int64_t rs = is_k ? k_rs : v_rs;
+    const uint32_t rs32 = is_k ? k_rs32 : v_rs32;
+    const uint8_t* base = uniform_ptr((is_k ? kbase : vbase) + static_cast<int64_t>(kt) * rs);
+    const uint32_t dst0 = lds_address(kbuf(t) + (is_k ? 0 : kKTile));
+    const int n_instr = is_k ? kKInstr : kVInstr;
+    const bool full = kt + kBN <= Lk;
+#pragma unroll
+    for (int j = 0; j < (is_k ? kPerK : kPerV); ++j) {
       const int i = wave + j * kWaves;  // wave-uniform
-      if (i < kInstr) {
-        const uint32_t row = static_cast<uint32_t>(min(kt + static_cast<int>(dma_rc[j] >> 16), Lk - 1));
-        const uint32_t col = dma_rc[j] & 0xFFFFu;
-        const bool is_k = i < kKInstr;
-        const uint8_t* src = is_k ? kbase + (row * k_rs32 + col) : vbase + (row * v_rs32 + col);
-        uint8_t* dst = buf + (is_k ? i * 1024 : kKTile + (i - kKInstr) * 1024);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      if (i < n_instr) {
+        uint32_t off = is_k ? dma_off_k[j] : dma_off_v[j < kPerV ? j : 0];
+        if (!full) {  // ragged last tile: rows past the sequence re-read its last row
+          const int2 rc = dma_row(j, is_k);
+          off = static_cast<uint32_t>(min(rc.x, Lk - 1 - kt)) * rs32 + static_cast<uint32_t>(rc.y);
+        }
+        dma_load16(base, off, dst0 + 1024u * static_cast<uint32_t>(i));
       }
     }
   };
@@ -259,51 +342,62 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   // transposed-read addresses (see the header): lane -> (16-lane group, source slot)
   const int grp = lane >> 4, slot = lane & 15;
   const int tb = slot >> 1, tp = slot & 1;
-  int vt_off[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int key = 16 * r + 8 * (tb >> 2) + 4 * (grp >> 1) + (tb & 3);
-    vt_off[r] = key * kVStride + 16 * (grp & 1) + 8 * tp;
-  }
+  // key of read r (r = 0..3) is 16 r + key0; the 16 r part is an immediate offset
+  // (keys vt_key0 + 16 r share the swizzle; block db of 32 dims flips address bits 5..6)
+  const int vt_key0 = 8 * (tb >> 2) + 4 * (grp >> 1) + (tb & 3);
+  const int vt_off = vt_key0 * kVStride + 16 * ((grp & 1) ^ v_swizzle(vt_key0)) + 8 * tp;
 
-  // prologue: tiles 0 and 1 in LDS, S of tile 0 computed
-  if (n_tiles > 0) issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
-  __syncthreads();
+  // prologue: K(0), V(0), K(1) in LDS, K(2) in flight, S of tile 0 computed
+  int in_flight = 0;
+  if (n_tiles > 0) { issue(0, true); issue(0, false); }
+  if (n_tiles > 1) issue(1, true);
+  if (n_tiles > 2) { issue(2, true); in_flight += n_k_instr; }
+  wait_vmcnt(in_flight);
+  // retire the Q-fragment loads here on every path (an empty asm that reads the
+  // registers), so that no compiler-inserted memory wait is left inside the loop
+#pragma unroll
+  for (int kb = 0; kb < 3; ++kb) asm volatile("" ::"v"(qf[kb]));
+  block_barrier();
   v16f s_cur[2];
   if (wave_tiles > 0) qk_tile(kbuf(0), col, g, qf, s_cur);
 
-  // Softmax of one group of 4 keys (w = 0..7) of this lane's 32: P' = 2^(c*s + nbias);
-  // hi = P' truncated to 3 mantissa bits (exact in E4M3 for P' >= 2^-6; below that the
-  // conversion rounds it, an error under 2^-10), packed into phi[w]; lo = P' - hi kept
-  // in fp32 for the second term; the row sum accumulates the fp32 P'.
-  auto softmax_group = [&](const v16f(&sc)[2], float nbias, int w, v8i& phi, float(&lo)[32]) {
+  // Softmax of one group of 4 keys (w = 0..7) of this lane's 32: P = 2^(c*s + nbias) <= 2^slack,
+  // rounded toward zero to f16 pairs. The f16 bit pattern of P read at bits 7..14 is the
+  // E4M3 code of 256 * P with its mantissa truncated to 3 bits (f16 and E4M3 exponent
+  // biases differ by 8, and f16 subnormals map onto E4M3 subnormals), so the hi term is
+  // a shift and a byte permute. lo = P - hi is exact in f16; its code is rounded to
+  // 3 mantissa bits (half away from zero) by adding 2^6 at bit 0 before the same
+  // extraction. hi + lo is 256 * P within 2^-7 relative; the row sum adds the f16 P.
+  auto softmax_group = [&](const v16f(&sc)[2], float nbias, int w, v8i& phi, v8i& plo) {
     float pw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = 4 * w + j;
       pw[j] = __builtin_amdgcn_exp2f(fmaf(sc[i >> 4][i & 15], c, nbias));
     }
-    l_run += (pw[0] + pw[1]) + (pw[2] + pw[3]);
-    const float h0 = trunc_e4m3(pw[0]), h1 = trunc_e4m3(pw[1]);
-    const float h2 = trunc_e4m3(pw[2]), h3 = trunc_e4m3(pw[3]);
-    const int hw = __builtin_amdgcn_cvt_pk_fp8_f32(h0, h1, 0, false);
-    phi[w] = __builtin_amdgcn_cvt_pk_fp8_f32(h2, h3, hw, true);
-    lo[4 * w + 0] = pw[0] - h0;
-    lo[4 * w + 1] = pw[1] - h1;
-    lo[4 * w + 2] = pw[2] - h2;
-    lo[4 * w + 3] = pw[3] - h3;
-  };
-  auto lo_group = [&](const float(&lo)[32], int w, v8i& plo) {
-    const int lw = __builtin_amdgcn_cvt_pk_fp8_f32(lo[4 * w + 0], lo[4 * w + 1], 0, false);
-    plo[w] = __builtin_amdgcn_cvt_pk_fp8_f32(lo[4 * w + 2], lo[4 * w + 3], lw, true);
+    const half2_t p01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]));
+    const half2_t p23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]));
+    l_run = __builtin_amdgcn_fdot2(p01, kOnes2, l_run, false);
+    l_run = __builtin_amdgcn_fdot2(p23, kOnes2, l_run, false);
+    const uint32_t u01 = __builtin_bit_cast(uint32_t, p01);
+    const uint32_t u23 = __builtin_bit_cast(uint32_t, p23);
+    // (u << 1) moves bits 7..14 of each half to bytes 1 and 3
+    phi[w] = static_cast<int>(__builtin_amdgcn_perm(u23 << 1, u01 << 1, 0x07050301u));
+    const half2_t lo01 = p01 - __builtin_bit_cast(half2_t, u01 & 0xFF80FF80u);
+    const half2_t lo23 = p23 - __builtin_bit_cast(half2_t, u23 & 0xFF80FF80u);
+    const uint32_t r01 = (__builtin_bit_cast(uint32_t, lo01) << 1) + 0x00800080u;
+    const uint32_t r23 = (__builtin_bit_cast(uint32_t, lo23) << 1) + 0x00800080u;
+    plo[w] = static_cast<int>(__builtin_amdgcn_perm(r23, r01, 0x07050301u));
+    // pin the group here: its results are only read in the next iteration, and the
+    // compiler would otherwise sink it below the MFMAs it is meant to overlap
+    asm volatile("" ::"v"(phi[w]), "v"(plo[w]), "v"(l_run));
   };
   auto vt_operand = [&](const uint8_t* vl, int db) {
-    const uint8_t* vp = vl + 32 * db;
-    const v2i r0 = read_tr8(vp + vt_off[0]);
-    const v2i r1 = read_tr8(vp + vt_off[1]);
-    const v2i r2 = read_tr8(vp + vt_off[2]);
-    const v2i r3 = read_tr8(vp + vt_off[3]);
+    const uint8_t* vp = vl + (vt_off ^ (db << 5));
+    const v2i r0 = read_tr8(vp);
+    const v2i r1 = read_tr8(vp + 16 * kVStride);
+    const v2i r2 = read_tr8(vp + 32 * kVStride);
+    const v2i r3 = read_tr8(vp + 48 * kVStride);
     return v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
   };
   // K operand of S MFMA k (k = 0..5 alternates the two 32-key blocks: consecutive MFMAs
@@ -312,54 +406,42 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     const int b2 = k & 1, kb = k >> 1;
     return load32(kl + (32 * b2 + col) * kKStride + 64 * kb + 32 * g);
   };
-  // PV of one tile: each hi MFMA is followed by a quarter of the lo conversion, then the
-  // lo MFMAs (V^T read again rather than kept in registers).
-  auto pv_tile = [&](const uint8_t* vl, const v8i& phi, const float(&lo)[32]) {
-    v8i plo;
-    v8i va = vt_operand(vl, 0);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      v8i vn;
-      if (db < 3) vn = vt_operand(vl, db + 1);
-      o[db] = mfma_f8(va, phi, o[db]);
-      __builtin_amdgcn_sched_barrier(0);
-      lo_group(lo, 2 * db, plo);
-      lo_group(lo, 2 * db + 1, plo);
-      __builtin_amdgcn_sched_barrier(0);
-      if (db < 3) va = vn;
-    }
-    asm volatile("" ::: "memory");  // re-read V^T below instead of keeping it live
-    va = vt_operand(vl, 0);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      v8i vn;
-      if (db < 3) vn = vt_operand(vl, db + 1);
-      o[db] = mfma_f8(va, plo, o[db]);
-      if (db < 3) va = vn;
-    }
-  };
+  // One software-pipelined iteration. S of tile it is in s_cur, the E4M3 P of tile it-1
+  // in (phi_p, plo_p). The iteration interleaves three independent streams: the 8 PV
+  // MFMAs of tile it-1 (hi and lo term of each 32-dim block), the 6 S MFMAs of tile it+1
+  // and the softmax of tile it, whose P goes to (phi_c, plo_c). A wave runs
+  // wave_tiles + 1 iterations: the last one is a fully masked tile that only completes
+  // the PV of the wave's last tile; on iteration 0 the previous P is zero (the PV adds
+  // nothing). S computed from a buffer past the wave's range is never used.
+  auto step = [&](int it, v16f(&s_cur)[2], v16f(&s_next)[2], const v8i& phi_p, const v8i& plo_p,
+                  v8i& phi_c, v8i& plo_c) {
+    int issued = 0;
+    if (it + 3 < n_tiles) { issue(it + 3, true); issued += n_k_instr; }
+    if (it + 1 < n_tiles) { issue(it + 1, false); issued += n_v_instr; }
 
-  // one pipelined iteration: S of tile it is in s_cur; S of tile it + 1 goes to s_next
-  auto step = [&](int it, v16f(&s_cur)[2], v16f(&s_next)[2]) {
-    // buffer (it + 2) % 3 held tile it - 1, which every wave finished before the last barrier
-    if (it + 2 < n_tiles) issue_tile(it + 2);
-    const bool cur = it < wave_tiles;
-    const bool nxt = it + 1 < wave_tiles;
+    if (it < wave_iters) {
+      const uint8_t* kl = kbuf(it + 1);
+      const uint8_t* vl = kbuf(it > 0 ? it - 1 : 0) + kKTile;
+      v8i va0 = vt_operand(vl, 0);
+      v8i va1 = vt_operand(vl, 1);
+      o[0] = mfma_f8(va0, phi_p, o[0]);
+      o[1] = mfma_f8(va1, phi_p, o[1]);
+      __builtin_amdgcn_sched_barrier(0);
 
-    float nbias = 0.f;
-    if (cur) {
       const int kt = it * kBN;
-      const bool need_mask = (kt + kBN > Lk) || (causal && kt + kBN - 1 > wrow0 + off);
+      const bool need_mask =
+          it >= wave_tiles || (kt + kBN > Lk) || (causal && kt + kBN - 1 > wrow0 + off);
       if (need_mask) {
         // side-effect barrier: keeps this rare block a real branch (the compiler would
         // otherwise if-convert it into selects executed on every tile)
         asm volatile("" ::: "memory");
+        const bool all = it >= wave_tiles;  // the trailing tile: nothing visible
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kt + 32 * b2 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= Lk || (causal && key > my_row + off)) s_cur[b2][r] = -INFINITY;
+            if (all || key >= Lk || (causal && key > my_row + off)) s_cur[b2][r] = -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -372,62 +454,93 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
         mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
       const float m_tile = mx * c;  // c > 0; -inf stays -inf
-      // Lazy rescale: keep the reference max m_run unless some row's max exceeds it
-      // by more than kRescaleSlack; then P' <= 2^(8 + slack) < 448 stays in E4M3.
-      if (__any(m_tile > m_run + kRescaleSlack)) {
+      // Lazy rescale: keep the reference max m_run unless some row's max exceeds it by
+      // more than kRescaleSlack. The row sum is rescaled now; O after the PV of the
+      // previous tile (computed against the old reference) has been added.
+      const bool rescale = __any(m_tile > m_run + kRescaleSlack);
+      float alpha = 1.f;
+      if (rescale) {
         asm volatile("" ::: "memory");  // keep the rescale a real branch (see above)
         const float m_new = fmaxf(m_run, m_tile);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while m_run is -inf
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 0 while m_run is -inf
         l_run *= alpha;
         m_run = m_new;
       }
-      nbias = kPScaleLog2 - ((m_run == -INFINITY) ? 0.f : m_run);
-    }
+      const float nbias = (m_run == -INFINITY) ? 0.f : -m_run;
+      __builtin_amdgcn_sched_barrier(0);
 
-    if (cur && nxt) {
-      // the S MFMAs of the next tile, each followed by one or two softmax groups of this
-      // tile; the K operand of MFMA k+1 is read while MFMA k runs
-      const uint8_t* kl = kbuf(it + 1);
-      v8i phi;
-      float lo[32];
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s_next[b2][r] = 0.f;
       v8i ka = k_operand(kl, 0);
+      v8i kb = k_operand(kl, 1);
+      v8i va2 = vt_operand(vl, 2);
+      s_next[0] = mfma_f8(ka, qf[0], s_next[0]);  // S, keys 0-31, dims 0-63
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_group(s_cur, nbias, 0, phi_c, plo_c);
+      __builtin_amdgcn_sched_barrier(0);
+      ka = k_operand(kl, 2);
+      o[0] = mfma_f8(va0, plo_p, o[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_group(s_cur, nbias, 1, phi_c, plo_c);
+      __builtin_amdgcn_sched_barrier(0);
+      v8i va3 = vt_operand(vl, 3);
+      s_next[1] = mfma_f8(kb, qf[0], s_next[1]);  // S, keys 32-63, dims 0-63
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_group(s_cur, nbias, 2, phi_c, plo_c);
+      __builtin_amdgcn_sched_barrier(0);
+      kb = k_operand(kl, 3);
+      o[2] = mfma_f8(va2, phi_p, o[2]);
+      __builtin_amdgcn_sched_barrier(0);
+      s_next[0] = mfma_f8(ka, qf[1], s_next[0]);  // dims 64-127
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_group(s_cur, nbias, 3, phi_c, plo_c);
+      __builtin_amdgcn_sched_barrier(0);
+      ka = k_operand(kl, 4);
+      o[1] = mfma_f8(va1, plo_p, o[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_group(s_cur, nbias, 4, phi_c, plo_c);
+      __builtin_amdgcn_sched_barrier(0);
+      s_next[1] = mfma_f8(kb, qf[1], s_next[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      kb = k_operand(kl, 5);
+      o[3] = mfma_f8(va3, phi_p, o[3]);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_group(s_cur, nbias, 5, phi_c, plo_c);
+      __builtin_amdgcn_sched_barrier(0);
+      s_next[0] = mfma_f8(ka, qf[2], s_next[0]);  // dims 128-191
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_group(s_cur, nbias, 6, phi_c, plo_c);
+      __builtin_amdgcn_sched_barrier(0);
+      o[2] = mfma_f8(va2, plo_p, o[2]);
+      __builtin_amdgcn_sched_barrier(0);
+      s_next[1] = mfma_f8(kb, qf[2], s_next[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_group(s_cur, nbias, 7, phi_c, plo_c);
+      __builtin_amdgcn_sched_barrier(0);
+      o[3] = mfma_f8(va3, plo_p, o[3]);
+
+      if (rescale) {
+        // alpha passes through an opaque asm so that the multiplies stay in this rare
+        // branch (alpha is 1 on the other path, which would let them be speculated)
+        asm volatile("" : "+v"(alpha)::"memory");
 #pragma unroll
-      for (int k = 0; k < 6; ++k) {
-        v8i kn;
-        if (k < 5) kn = k_operand(kl, k + 1);
-        s_next[k & 1] = mfma_f8(ka, qf[k >> 1], s_next[k & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        softmax_group(s_cur, nbias, k, phi, lo);                  // groups 0..5
-        if (k >= 4) softmax_group(s_cur, nbias, k + 2, phi, lo);  // groups 6, 7
-        __builtin_amdgcn_sched_barrier(0);
-        if (k < 5) ka = kn;
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
-      pv_tile(kbuf(it) + kKTile, phi, lo);
-    } else if (cur) {
-      v8i phi;
-      float lo[32];
-#pragma unroll
-      for (int w = 0; w < 8; ++w) softmax_group(s_cur, nbias, w, phi, lo);
-      pv_tile(kbuf(it) + kKTile, phi, lo);
-    } else if (nxt) {
-      qk_tile(kbuf(it + 1), col, g, qf, s_next);
     }
-    __syncthreads();
+    wait_vmcnt(issued);  // K(it+2) and V(it) have landed; this iteration's loads may fly
+    block_barrier();
   };
 
   v16f s_alt[2];
-  for (int it = 0; it < n_tiles; it += 2) {
-    step(it, s_cur, s_alt);
-    if (it + 1 < n_tiles) step(it + 1, s_alt, s_cur);
+  v8i phi_a = {0, 0, 0, 0, 0, 0, 0, 0}, plo_a = phi_a, phi_b = phi_a, plo_b = phi_a;
+  for (int it = 0; it <= n_tiles; it += 2) {
+    step(it, s_cur, s_alt, phi_a, plo_a, phi_b, plo_b);
+    if (it + 1 <= n_tiles) step(it + 1, s_alt, s_cur, phi_b, plo_b, phi_a, plo_a);
   }
 
   // epilogue: this lane holds row my_row, dims 32*db + 8*(r/4) + 4*g + r%4
@@ -438,7 +551,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
   if (row_ok) {
-    const float inv = (l_tot > 0.f) ? p.dv[h] / l_tot : 0.f;
+    // O holds 256 * sum P v (the E4M3 codes of P are 256 * P)
+    const float inv = (l_tot > 0.f) ? p.dv[h] / (256.f * l_tot) : 0.f;
     const int64_t obase = (q0 + my_row) * (static_cast<int64_t>(H) * kDv) + h * kDv;
     if (p.out_f32) {
       float* op = static_cast<float*>(p.out) + obase;
@@ -465,7 +579,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     }
     if (g == 0 && p.lse != nullptr)
       p.lse[static_cast<int64_t>(h) * p.lse_stride + q0 + my_row] =
-          (l_tot > 0.f) ? (m_run + __log2f(l_tot) - kPScaleLog2) * kLn2 : -INFINITY;
+          (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
