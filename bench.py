@@ -37,11 +37,16 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the HIP sources with // comments and blank lines removed, so that the
+    counter record stays valid across comment-only edits."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_mla_context_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, fn), "rb") as f:
-            h.update(fn.encode() + f.read())
+        with open(os.path.join(csrc, fn)) as f:
+            text = f.read()
+        code = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
+        h.update(fn.encode() + "\n".join(line for line in code if line).encode())
     return h.hexdigest()[:16]
 
 
@@ -58,8 +63,9 @@ def load_traffic(kernel_hash: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, codes_np, ds, n_rows: int, seed: int = 1):
-    """The oracle, as it stands, on a bounded sample of the workload's query rows."""
+def cpu_baseline(wl, codes_np, ds, target_s: float, seed: int = 1):
+    """The oracle, as it stands, on a bounded sample of the workload's query rows, sized by
+    two shorter runs so that the reported run takes about target_s."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -67,20 +73,30 @@ def cpu_baseline(wl, codes_np, ds, n_rows: int, seed: int = 1):
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
     rng = np.random.default_rng(seed)
-    rows = np.sort(rng.choice(wl.total_q, size=n_rows, replace=False))
-    t0 = time.perf_counter()
-    oracle.attention_rows(codes_np[0], codes_np[1], codes_np[2], wl.cu_seqlens_q,
-                          wl.cu_seqlens_k, ds[0], ds[1], ds[2], wl.softmax_scale, wl.causal, rows)
-    dt = time.perf_counter() - t0
+
+    def run(n_rows):
+        rows = np.sort(rng.choice(wl.total_q, size=n_rows, replace=False))
+        t0 = time.perf_counter()
+        oracle.attention_rows(codes_np[0], codes_np[1], codes_np[2], wl.cu_seqlens_q,
+                              wl.cu_seqlens_k, ds[0], ds[1], ds[2], wl.softmax_scale, wl.causal,
+                              rows)
+        return rows, time.perf_counter() - t0
+
+    # size the sample in two steps (a short probe, then a third of the target)
+    n_rows = 128
+    _, dt = run(n_rows)
+    for frac in (1.0 / 3.0, 1.0):
+        n_rows = int(min(wl.total_q, max(n_rows, n_rows * frac * target_s / max(dt, 1e-3))))
+        rows, dt = run(n_rows)
     # visible keys of each sampled row (single causal sequence, Lq == Lk)
-    lq = wl.total_q
-    lk = wl.total_k
+    lq, lk = wl.total_q, wl.total_k
     vis = np.minimum(lk, rows + (lk - lq) + 1) if wl.causal else np.full(n_rows, lk)
     flop = float(np.sum(vis)) * wl.q.shape[1] * FLOP_PER_PAIR
     return {
         "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"{n_rows} seeded query rows x {wl.q.shape[1]} heads of {wl.name}, fp64 NumPy "
-                  f"oracle attention on the dequantized FP8 inputs, {dt:.1f} s",
+        "sample": f"{n_rows} seeded query rows x {wl.q.shape[1]} heads of {wl.name} "
+                  f"({float(np.sum(vis)):.3g} visible pairs per head), fp64 NumPy oracle "
+                  f"attention on the dequantized FP8 inputs, {dt:.1f} s",
         "seconds": dt,
     }
 
@@ -91,7 +107,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="C3")
-    ap.add_argument("--cpu-rows", type=int, default=384, help="query rows for the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the timed oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
@@ -239,7 +256,7 @@ def main(argv=None):
         codes_np = [c.cpu().numpy() for c in codes]
         ds_np = [d.cpu().numpy() for d in descales]
         log("[bench] timing the CPU oracle on a sample ...")
-        cb = cpu_baseline(wl, codes_np, ds_np, args.cpu_rows)
+        cb = cpu_baseline(wl, codes_np, ds_np, args.cpu_seconds)
         log(f"[bench] cpu oracle: {cb['value'] * 1e3:.2f} GFLOP/s on {cb['cores']} threads, "
             f"{cb['seconds']:.1f} s")
         result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}

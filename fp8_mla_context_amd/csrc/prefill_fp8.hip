@@ -6,43 +6,40 @@
 // Q/K/V); the close comment separates causal and non-causal shapes.
 //
 // Design (gfx950, wave64):
-//  * One workgroup = 4 waves = 128 query rows of one (sequence, head); each
-//    wave owns 32 rows; two workgroups share a CU (two waves per SIMD from
-//    independent workgroups, so one's barrier stalls are covered by the other). Workgroups are ordered heaviest first: the flattened
-//    block index walks query tiles from the last (most keys under a causal
-//    mask) to the first, with heads and sequences fastest.
-//  * K/V tiles of 64 keys are staged in LDS in their natural [key][dim]
-//    layout in three rotating buffers, filled by direct global->LDS loads (no
-//    register staging). The loop is software-pipelined: in iteration t a wave
-//    starts the loads of tile t+2, issues the S MFMAs of tile t+1, runs the
-//    softmax of tile t on the VALU while those execute, and issues the PV
-//    MFMAs of tile t as soon as each half of P is ready. One barrier per tile.
-//  * S^T = K * Q^T on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32): the
-//    Q fragment (32 rows x 192) stays in registers as the B operand, K rows
-//    are read from LDS as the A operand. In the 32x32 accumulator layout every
-//    lane then holds one query row (lane % 32) and 32 of the tile's keys, so
-//    the row max needs one cross-lane step (lane ^ 32) and row sums stay per
-//    lane until the end.
-//  * Online softmax in base 2: c = dq*dk*softmax_scale*log2(e) > 0, so the
-//    tile max is taken on raw logits and scaled once; P' = 2^(c*s - m + 8)
-//    is one FMA and one v_exp_f32 per element (pre-scaled by 2^8 so small
-//    weights stay out of E4M3 subnormals). O and l are rescaled only when
-//    some row's running max grew (a wave-uniform branch).
-//  * O^T = V^T * P^T on the same MFMA: P' is split in two E4M3 terms,
-//    hi = E4M3(P') (round to nearest even) and lo = E4M3(P' - hi), both
-//    accumulated into the same fp32 O; one E4M3 term would carry ~2.5%
-//    relative error per weight, which the output tolerance does not allow on
-//    diffuse heads. The accumulator layout of S^T already is the B operand
-//    (lane = query row, bytes = 32 keys). The V^T A operand comes from
-//    ds_read_b64_tr_b8: within each 16-lane group, output lane i receives byte
-//    i % 8 of the 8-byte windows addressed by lanes 2b + i/8 (b = 0..7); with
-//    lanes 2b and 2b+1 pointing at the same key row and at dims d0 and d0 + 8,
-//    lane i gets dim d0 + i of 8 keys, in the key order of the P operand.
+//  * One workgroup = 4 waves = 128 query rows of one (sequence, head); each wave owns
+//    32 rows. Two workgroups share a CU, so each SIMD runs two waves from different
+//    workgroups and one's VALU work fills the other's MFMA time. Workgroups are ordered
+//    heaviest first: the flattened block index walks query tiles from the last (most
+//    keys under a causal mask) to the first, with heads and sequences fastest.
+//  * 64-key K/V tiles live in three rotating LDS buffers, filled by global->LDS DMA
+//    (global_load_lds_dwordx4, no register staging). K rows are padded to 208 bytes; V
+//    rows are 128 bytes with XOR-swizzled 16-byte chunks (see v_swizzle). Iteration t
+//    issues the loads of K(t+3) and V(t+1) and computes, interleaved, the PV MFMAs of
+//    tile t-1, the S MFMAs of tile t+1 and the softmax of tile t. One barrier per tile.
+//  * S^T = K * Q^T on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32): the Q fragment
+//    (32 rows x 192) stays in registers as the B operand, K rows are read from LDS as
+//    the A operand. In the 32x32 accumulator layout every lane holds one query row
+//    (lane % 32) and 32 of the tile's keys, so a row max needs one cross-lane step
+//    (lane ^ 32) and row sums stay per lane until the end.
+//  * Online softmax in base 2: c = dq*dk*softmax_scale*log2(e) > 0, so the tile max is
+//    taken on raw logits and scaled once; P = 2^(c*s - m) is one FMA and one v_exp_f32
+//    per element. The reference max m moves only when a row's max exceeds it by more
+//    than kRescaleSlack (a rare wave-uniform branch rescales l, and O once the previous
+//    tile's PV has been added).
+//  * O^T = V^T * P^T on the same MFMA with P in two E4M3 terms (hi + lo, both summed
+//    into the same fp32 O): one E4M3 term carries up to 2^-4 relative error per weight,
+//    which the output tolerance does not allow on diffuse heads. The split uses f16 bit
+//    arithmetic (see softmax_group). The accumulator layout of S^T already is the B
+//    operand (lane = query row, bytes = 32 keys). The V^T A operand comes from
+//    ds_read_b64_tr_b8: within each 16-lane group, output lane i receives byte i % 8 of
+//    the 8-byte windows addressed by lanes 2b + i/8 (b = 0..7); with lanes 2b and 2b+1
+//    pointing at the same key row and at dims d0 and d0 + 8, lane i gets dim d0 + i of
+//    8 keys, in the key order of the P operand.
 //  * Causal (bottom-right aligned: key j visible to row i iff j <= i + Lk - Lq):
 //    a wave skips tiles past its last visible key; only tiles that cross the
 //    diagonal or the ragged end are masked element-wise.
-//  * Epilogue: out = O * dv / l in bf16 (fp32 for the partials of a chunked
-//    pass), lse = ln2 * (m + log2 l - 8).
+//  * Epilogue: out = O * dv / (256 l) in bf16 (fp32 for the partials of a chunked pass),
+//    lse = ln2 * (m + log2 l).
 #include "mla_internal.h"
 
 namespace {
