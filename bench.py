@@ -1,12 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of FP8 MLA context prefill on one MI355X.
 
-One step = the whole hot path over one batch of synthetic input that is
-already resident in HBM: the one-launch static quantizer over Q, K and V,
-then the FP8 varlen prefill (the 32K-token causal workload is a single
-segment, so there is nothing to merge). The headline value is causal-counted
-TFLOP/s of the step: 640 FLOP per visible (query, key) pair and head, with
-640 = 2 * (192 + 128).
+One step = the whole hot path over one batch of synthetic input that is already
+resident in HBM. For the default 32K-token causal workload (C3, a single segment)
+that is the one-launch static quantizer over Q, K and V, then the FP8 varlen
+prefill. For the chunked workloads (C4, C5) it is the quantizer, then the chunked
+prefill (one prefill launch per (query chunk, context segment) and the LSE merges).
+The headline value is causal-counted TFLOP/s of the step: 640 FLOP per visible
+(query, key) pair and head, with 640 = 2 * (192 + 128).
 
 Prints ONE JSON line on stdout. Everything else goes to stderr.
 """
@@ -16,7 +17,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -27,7 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "causal TFLOP/s + % FP8 MFMA peak, MLA D192/V128 12-head varlen prefill"
-FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, published (at 2.4 GHz)
+PEAK_CLOCK_GHZ = 2.4
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 FLOP_PER_PAIR = 2 * (192 + 128)
 
@@ -50,17 +51,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_hash: str):
-    """HBM bytes per prefill launch from committed PMC counters, if they were taken
-    on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "prefill_c3_traffic.json")
+def load_counters(kernel_hash: str, workload: str):
+    """Per-launch counter record of the prefill (HBM bytes, GPU clock cycles) for this
+    workload, if it was taken on the current kernel sources; else an empty dict."""
+    path = os.path.join(ROOT, "profiles", f"prefill_{workload.lower()}_counters.json")
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_hash") != kernel_hash:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec if rec.get("kernel_hash") == kernel_hash else {}
 
 
 def cpu_baseline(wl, codes_np, ds, target_s: float, seed: int = 1):
@@ -88,7 +87,7 @@ def cpu_baseline(wl, codes_np, ds, target_s: float, seed: int = 1):
     for frac in (1.0 / 3.0, 1.0):
         n_rows = int(min(wl.total_q, max(n_rows, n_rows * frac * target_s / max(dt, 1e-3))))
         rows, dt = run(n_rows)
-    # visible keys of each sampled row (single causal sequence, Lq == Lk)
+    # visible keys of each sampled row (one sequence: the last Lq of Lk tokens)
     lq, lk = wl.total_q, wl.total_k
     vis = np.minimum(lk, rows + (lk - lq) + 1) if wl.causal else np.full(n_rows, lk)
     flop = float(np.sum(vis)) * wl.q.shape[1] * FLOP_PER_PAIR
@@ -101,17 +100,32 @@ def cpu_baseline(wl, codes_np, ds, target_s: float, seed: int = 1):
     }
 
 
+def event_ms(torch, fn, reps: int, stream):
+    """Mean and minimum duration of fn() over reps launches, timed with HIP events recorded
+    on the launch stream around each launch."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    return float(np.mean(t)), float(np.min(t))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="C3")
+    ap.add_argument("--workload", default="C3", choices=["C3", "C4", "C5"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the timed oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also run a plain device copy of this size (counter calibration)")
+                    help="also run an elementwise read+write kernel of this size (counter "
+                         "calibration and practical HBM roofline)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -132,6 +146,7 @@ def main(argv=None):
     t_gen = time.perf_counter()
     wl = make_workload(args.workload)
     heads = wl.q.shape[1]
+    chunked = wl.segment_len > 0
     log(f"[bench] workload {wl.name}: {wl.description}; generated in "
         f"{time.perf_counter() - t_gen:.1f} s")
 
@@ -153,14 +168,25 @@ def main(argv=None):
     cu_k = torch.from_numpy(wl.cu_seqlens_k).cuda()
     out = torch.empty((wl.total_q, heads, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((heads, wl.total_q), dtype=torch.float32, device="cuda")
+    workspace = None
+    if chunked:
+        need = B.chunked_workspace_size(wl.total_q, wl.total_k, heads, wl.segment_len, wl.causal)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def quant():
         B.quant_static([q, k, v], descales, outs=codes)
 
-    def prefill():
+    def prefill_single():
         B.prefill_varlen(codes[0], codes[1], codes[2], cu_q, cu_k, wl.max_seqlen_q,
                          wl.max_seqlen_k, descales[0], descales[1], descales[2], wl.softmax_scale,
                          wl.causal, out=out, lse=lse)
+
+    def prefill_chunked():
+        B.prefill_chunked(codes[0], codes[1], codes[2], descales[0], descales[1], descales[2],
+                          wl.softmax_scale, wl.segment_len, wl.causal, out=out, lse=lse,
+                          workspace=workspace)
+
+    prefill = prefill_chunked if chunked else prefill_single
 
     def step():
         quant()
@@ -188,20 +214,45 @@ def main(argv=None):
 
     # per-kernel durations with HIP events on the launch stream (torch's current stream)
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for e in ev:
-        e[0].record(stream)
-        quant()
-        e[1].record(stream)
-        prefill()
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    prefill_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    prefill_min = float(np.min([e[1].elapsed_time(e[2]) for e in ev]))
+    reps = max(args.steps, 3)
+    quant_ms, _ = event_ms(torch, quant, reps, stream)
+    prefill_ms, prefill_min = event_ms(torch, prefill, reps, stream)
     achieved = flop / (prefill_ms * 1e-3) / 1e12
+    what = "chunked prefill (all segments + merges)" if chunked else "prefill"
     log(f"[bench] event timing: quant {quant_ms * 1e3:.1f} us ({quant_bytes / quant_ms / 1e6:.0f} GB/s), "
-        f"prefill {prefill_ms:.3f} ms (min {prefill_min:.3f}) = {achieved:.1f} TFLOP/s")
+        f"{what} {prefill_ms:.3f} ms (min {prefill_min:.3f}) = {achieved:.1f} TFLOP/s")
+
+    kernels = {
+        "quant_static_us": round(quant_ms * 1e3, 2),
+        "quant_static_GBps": round(quant_bytes / quant_ms / 1e6, 1),
+    }
+    if chunked:
+        kernels["chunked_prefill_ms"] = round(prefill_ms, 4)
+        kernels["pipeline_ms"] = round(quant_ms + prefill_ms, 4)
+        # the same attention as one unsegmented bottom-right causal call
+        single_ms, _ = event_ms(torch, prefill_single, reps, stream)
+        kernels["unsegmented_prefill_ms"] = round(single_ms, 4)
+        kernels["unsegmented_TFLOPs"] = round(flop / (single_ms * 1e-3) / 1e12, 2)
+        # the public merge on as many bf16 partials as the last query chunk combines
+        seg = wl.segment_len
+        n_parts = min(64, (wl.total_k + seg - 1) // seg)
+        rows = min(wl.total_q, seg)
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        parts = [torch.randn((rows, heads, 128), device="cuda", generator=gen).to(torch.bfloat16)
+                 for _ in range(n_parts)]
+        lses = [torch.randn((heads, rows), device="cuda", generator=gen) for _ in range(n_parts)]
+        m_out = torch.empty_like(parts[0])
+        m_lse = torch.empty_like(lses[0])
+        merge_ms, _ = event_ms(torch, lambda: B.merge_lse(parts, lses, out=m_out, lse_out=m_lse),
+                               reps, stream)
+        merge_bytes = (n_parts + 1) * rows * heads * (128 * 2 + 4)
+        kernels["merge_lse"] = {"partials": n_parts, "rows": rows, "us": round(merge_ms * 1e3, 2),
+                                "bytes": merge_bytes,
+                                "GBps": round(merge_bytes / merge_ms / 1e6, 1)}
+        log(f"[bench] unsegmented prefill {single_ms:.3f} ms; merge of {n_parts} bf16 partials x "
+            f"{rows} rows: {merge_ms * 1e3:.1f} us ({merge_bytes / merge_ms / 1e6:.0f} GB/s)")
+    else:
+        kernels["prefill_ms"] = round(prefill_ms, 4)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20)
@@ -211,10 +262,30 @@ def main(argv=None):
             # an elementwise kernel (a plain D2D copy may go to the DMA engine, which the
             # kernel counters do not see): reads n bytes, writes n bytes
             torch.mul(src, 1, out=dst)
-        torch.cuda.synchronize()
-        log(f"[bench] copy probe: elementwise kernel reading {n} B and writing {n} B, 3 launches")
+        probe_ms, _ = event_ms(torch, lambda: torch.mul(src, 1, out=dst), 5, stream)
+        kernels["copy_probe_GBps"] = round(2 * n / probe_ms / 1e6, 1)
+        log(f"[bench] elementwise probe: {2 * n} B moved in {probe_ms:.3f} ms "
+            f"({2 * n / probe_ms / 1e6:.0f} GB/s, the practical HBM roofline)")
 
     khash = kernel_source_hash()
+    rec = load_counters(khash, wl.name)
+    roofline = {
+        "bound": "mfma",
+        "kernel": "prefill_fp8_kernel" + (" (+ merge_lse_kernel, chunked)" if chunked else ""),
+        "achieved": round(achieved, 2),
+        "peak": FP8_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+        "traffic": rec.get("hbm_bytes_per_launch"),
+    }
+    if rec.get("gfx_cycles_per_launch") and not chunked:
+        # GPU clock during the launch = counted cycles / live duration
+        sclk = rec["gfx_cycles_per_launch"] / (prefill_ms * 1e-3) / 1e9
+        peak_adj = FP8_PEAK_TFLOPS * sclk / PEAK_CLOCK_GHZ
+        roofline["sclk_GHz"] = round(sclk, 3)
+        roofline["peak_clock_adjusted"] = round(peak_adj, 1)
+        roofline["frac_clock_adjusted"] = round(achieved / peak_adj, 4)
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -230,25 +301,14 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: {wl.description}",
-            "tokens": wl.total_q, "heads": heads, "head_dim_qk": 192, "head_dim_v": 128,
-            "causal": bool(wl.causal), "causal_flop": flop,
-            "step": "quant_static(Q,K,V) + prefill_varlen",
+            "tokens_q": wl.total_q, "tokens_k": wl.total_k, "heads": heads,
+            "head_dim_qk": 192, "head_dim_v": 128, "causal": bool(wl.causal),
+            "segment": wl.segment_len or None, "causal_flop": flop,
+            "step": "quant_static(Q,K,V) + " + ("prefill_chunked" if chunked else "prefill_varlen"),
         },
         "pct_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
-        "kernels": {
-            "quant_static_us": round(quant_ms * 1e3, 2),
-            "quant_static_GBps": round(quant_bytes / quant_ms / 1e6, 1),
-            "prefill_ms": round(prefill_ms, 4),
-        },
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "prefill_fp8_kernel",
-            "achieved": round(achieved, 2),
-            "peak": FP8_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-            "traffic": load_traffic(khash),
-        },
+        "kernels": kernels,
+        "roofline": roofline,
         "kernel_hash": khash,
     }
 

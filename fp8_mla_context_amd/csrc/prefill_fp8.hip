@@ -365,15 +365,17 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   // a shift and a byte permute. lo = P - hi is exact in f16; its code is rounded to
   // 3 mantissa bits (half away from zero) by adding 2^6 at bit 0 before the same
   // extraction. hi + lo is 256 * P within 2^-7 relative; the row sum adds the f16 P.
-  auto softmax_group = [&](const v16f(&sc)[2], float nbias, int w, v8i& phi, v8i& plo) {
-    float pw[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = 4 * w + j;
-      pw[j] = __builtin_amdgcn_exp2f(fmaf(sc[i >> 4][i & 15], c, nbias));
-    }
-    const half2_t p01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]));
-    const half2_t p23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]));
+  auto softmax_exp = [&](const v16f(&sc)[2], float nbias, int w) {
+    float4 pw;
+    pw.x = __builtin_amdgcn_exp2f(fmaf(sc[(4 * w) >> 4][(4 * w) & 15], c, nbias));
+    pw.y = __builtin_amdgcn_exp2f(fmaf(sc[(4 * w + 1) >> 4][(4 * w + 1) & 15], c, nbias));
+    pw.z = __builtin_amdgcn_exp2f(fmaf(sc[(4 * w + 2) >> 4][(4 * w + 2) & 15], c, nbias));
+    pw.w = __builtin_amdgcn_exp2f(fmaf(sc[(4 * w + 3) >> 4][(4 * w + 3) & 15], c, nbias));
+    return pw;
+  };
+  auto softmax_pack = [&](const float4& pw, int w, v8i& phi, v8i& plo) {
+    const half2_t p01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pw.x, pw.y));
+    const half2_t p23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pw.z, pw.w));
     l_run = __builtin_amdgcn_fdot2(p01, kOnes2, l_run, false);
     l_run = __builtin_amdgcn_fdot2(p23, kOnes2, l_run, false);
     const uint32_t u01 = __builtin_bit_cast(uint32_t, p01);
@@ -412,19 +414,24 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   // nothing). S computed from a buffer past the wave's range is never used.
   auto step = [&](int it, v16f(&s_cur)[2], v16f(&s_next)[2], const v8i& phi_p, const v8i& plo_p,
                   v8i& phi_c, v8i& plo_c) {
+    const bool active = it < wave_iters;
+    const uint8_t* kl = kbuf(it + 1);
+    const uint8_t* vl = kbuf(it > 0 ? it - 1 : 0) + kKTile;
+    // operands of the first MFMAs, read before anything else so that the loads below
+    // and the max reduction cover their latency
+    v8i va0, va1, va2, va3, ka, kb;
+    if (active) {
+      va0 = vt_operand(vl, 0);
+      va1 = vt_operand(vl, 1);
+      ka = k_operand(kl, 0);
+      kb = k_operand(kl, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     int issued = 0;
     if (it + 3 < n_tiles) { issue(it + 3, true); issued += n_k_instr; }
     if (it + 1 < n_tiles) { issue(it + 1, false); issued += n_v_instr; }
 
-    if (it < wave_iters) {
-      const uint8_t* kl = kbuf(it + 1);
-      const uint8_t* vl = kbuf(it > 0 ? it - 1 : 0) + kKTile;
-      v8i va0 = vt_operand(vl, 0);
-      v8i va1 = vt_operand(vl, 1);
-      o[0] = mfma_f8(va0, phi_p, o[0]);
-      o[1] = mfma_f8(va1, phi_p, o[1]);
-      __builtin_amdgcn_sched_barrier(0);
-
+    if (active) {
       const int kt = it * kBN;
       const bool need_mask =
           it >= wave_tiles || (kt + kBN > Lk) || (causal && kt + kBN - 1 > wrow0 + off);
@@ -465,59 +472,63 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
         m_run = m_new;
       }
       const float nbias = (m_run == -INFINITY) ? 0.f : -m_run;
-      __builtin_amdgcn_sched_barrier(0);
 
+      // 14 MFMA slots; each is followed by the exponentials of one softmax group (E) or
+      // the split and pack of the group whose exponentials were taken two slots earlier (P)
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s_next[b2][r] = 0.f;
-      v8i ka = k_operand(kl, 0);
-      v8i kb = k_operand(kl, 1);
-      v8i va2 = vt_operand(vl, 2);
-      s_next[0] = mfma_f8(ka, qf[0], s_next[0]);  // S, keys 0-31, dims 0-63
+      float4 e_a = softmax_exp(s_cur, nbias, 0);
       __builtin_amdgcn_sched_barrier(0);
-      softmax_group(s_cur, nbias, 0, phi_c, plo_c);
+      o[0] = mfma_f8(va0, phi_p, o[0]);                      // PV hi, dims 0-31
+      float4 e_b = softmax_exp(s_cur, nbias, 1);
       __builtin_amdgcn_sched_barrier(0);
+      s_next[0] = mfma_f8(ka, qf[0], s_next[0]);             // S, keys 0-31, dims 0-63
       ka = k_operand(kl, 2);
-      o[0] = mfma_f8(va0, plo_p, o[0]);
+      softmax_pack(e_a, 0, phi_c, plo_c);
       __builtin_amdgcn_sched_barrier(0);
-      softmax_group(s_cur, nbias, 1, phi_c, plo_c);
+      o[1] = mfma_f8(va1, phi_p, o[1]);                      // PV hi, dims 32-63
+      e_a = softmax_exp(s_cur, nbias, 2);
       __builtin_amdgcn_sched_barrier(0);
-      v8i va3 = vt_operand(vl, 3);
-      s_next[1] = mfma_f8(kb, qf[0], s_next[1]);  // S, keys 32-63, dims 0-63
-      __builtin_amdgcn_sched_barrier(0);
-      softmax_group(s_cur, nbias, 2, phi_c, plo_c);
-      __builtin_amdgcn_sched_barrier(0);
+      s_next[1] = mfma_f8(kb, qf[0], s_next[1]);             // S, keys 32-63, dims 0-63
       kb = k_operand(kl, 3);
-      o[2] = mfma_f8(va2, phi_p, o[2]);
+      softmax_pack(e_b, 1, phi_c, plo_c);
       __builtin_amdgcn_sched_barrier(0);
-      s_next[0] = mfma_f8(ka, qf[1], s_next[0]);  // dims 64-127
+      o[0] = mfma_f8(va0, plo_p, o[0]);                      // PV lo, dims 0-31
+      va2 = vt_operand(vl, 2);
+      e_b = softmax_exp(s_cur, nbias, 3);
       __builtin_amdgcn_sched_barrier(0);
-      softmax_group(s_cur, nbias, 3, phi_c, plo_c);
-      __builtin_amdgcn_sched_barrier(0);
+      s_next[0] = mfma_f8(ka, qf[1], s_next[0]);             // dims 64-127
       ka = k_operand(kl, 4);
-      o[1] = mfma_f8(va1, plo_p, o[1]);
+      softmax_pack(e_a, 2, phi_c, plo_c);
       __builtin_amdgcn_sched_barrier(0);
-      softmax_group(s_cur, nbias, 4, phi_c, plo_c);
+      o[1] = mfma_f8(va1, plo_p, o[1]);                      // PV lo, dims 32-63
+      va3 = vt_operand(vl, 3);
+      e_a = softmax_exp(s_cur, nbias, 4);
+      __builtin_amdgcn_sched_barrier(0);
+      o[2] = mfma_f8(va2, phi_p, o[2]);                      // PV hi, dims 64-95
+      softmax_pack(e_b, 3, phi_c, plo_c);
       __builtin_amdgcn_sched_barrier(0);
       s_next[1] = mfma_f8(kb, qf[1], s_next[1]);
-      __builtin_amdgcn_sched_barrier(0);
       kb = k_operand(kl, 5);
-      o[3] = mfma_f8(va3, phi_p, o[3]);
+      e_b = softmax_exp(s_cur, nbias, 5);
       __builtin_amdgcn_sched_barrier(0);
-      softmax_group(s_cur, nbias, 5, phi_c, plo_c);
+      o[3] = mfma_f8(va3, phi_p, o[3]);                      // PV hi, dims 96-127
+      softmax_pack(e_a, 4, phi_c, plo_c);
       __builtin_amdgcn_sched_barrier(0);
-      s_next[0] = mfma_f8(ka, qf[2], s_next[0]);  // dims 128-191
+      s_next[0] = mfma_f8(ka, qf[2], s_next[0]);             // dims 128-191
+      e_a = softmax_exp(s_cur, nbias, 6);
       __builtin_amdgcn_sched_barrier(0);
-      softmax_group(s_cur, nbias, 6, phi_c, plo_c);
-      __builtin_amdgcn_sched_barrier(0);
-      o[2] = mfma_f8(va2, plo_p, o[2]);
+      o[2] = mfma_f8(va2, plo_p, o[2]);                      // PV lo, dims 64-95
+      softmax_pack(e_b, 5, phi_c, plo_c);
       __builtin_amdgcn_sched_barrier(0);
       s_next[1] = mfma_f8(kb, qf[2], s_next[1]);
+      e_b = softmax_exp(s_cur, nbias, 7);
       __builtin_amdgcn_sched_barrier(0);
-      softmax_group(s_cur, nbias, 7, phi_c, plo_c);
-      __builtin_amdgcn_sched_barrier(0);
-      o[3] = mfma_f8(va3, plo_p, o[3]);
+      o[3] = mfma_f8(va3, plo_p, o[3]);                      // PV lo, dims 96-127
+      softmax_pack(e_a, 6, phi_c, plo_c);
+      softmax_pack(e_b, 7, phi_c, plo_c);
 
       if (rescale) {
         // alpha passes through an opaque asm so that the multiplies stay in this rare
