@@ -92,6 +92,7 @@ struct PrefillParams {
   int32_t n_m_tiles;
   int32_t causal;
   int32_t out_f32;  // 1: out is fp32 (partials of a chunked pass), 0: bf16
+  int32_t xcd_order;  // 1: XCD-aware block order (one sequence, H % 4 == 0, even tile count)
   float scale_log2;
 };
 
@@ -199,13 +200,30 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int H = p.n_heads;
 
-  // heaviest query tiles first; heads, then sequences, vary fastest
-  int idx = blockIdx.x;
-  const int h = idx % H;
-  idx /= H;
-  const int b = idx % p.batch;
-  idx /= p.batch;
-  const int m_tile = p.n_m_tiles - 1 - idx;
+  int h, b, m_tile;
+  if (p.xcd_order) {
+    // One sequence: workgroups are dealt round-robin to the 8 XCDs (block % 8). Each
+    // head's query tiles are split into an even and an odd half (equal causal work) and
+    // each XCD takes H/4 consecutive half-heads, heaviest tile first, so its L2 serves
+    // the K/V of about H/8 heads instead of H/4 spread over all XCDs. (A bijection of
+    // the grid whatever the dispatch order.)
+    const int hp = H >> 2;                 // half-heads per XCD
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    const int half = hp * xcd + slot % hp;  // 0 .. 2H-1
+    const int rank = slot / hp;             // 0 .. n_m/2 - 1
+    h = half >> 1;
+    b = 0;
+    m_tile = p.n_m_tiles - 2 + (half & 1) - 2 * rank;
+  } else {
+    // heaviest query tiles first; heads, then sequences, vary fastest
+    int idx = blockIdx.x;
+    h = idx % H;
+    idx /= H;
+    b = idx % p.batch;
+    idx /= p.batch;
+    m_tile = p.n_m_tiles - 1 - idx;
+  }
 
   // packed sequences from cu_seqlens, or one sequence spanning all tokens
   int64_t q0 = 0, q1 = p.total_q, k0 = 0, k1 = p.total_k;
@@ -622,6 +640,7 @@ int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   prm.n_m_tiles = static_cast<int32_t>(n_m);
   prm.causal = a.causal;
   prm.scale_log2 = a.softmax_scale * 1.44269504088896340736f;
+  prm.xcd_order = (a.batch == 1 && a.n_heads % 4 == 0 && n_m % 2 == 0) ? 1 : 0;
   hipLaunchKernelGGL(prefill_fp8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
                      stream, prm);
   return check_launch("prefill_fp8_kernel");
