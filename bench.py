@@ -226,6 +226,18 @@ def main(argv=None):
         "quant_static_us": round(quant_ms * 1e3, 2),
         "quant_static_GBps": round(quant_bytes / quant_ms / 1e6, 1),
     }
+    # the dynamic per-head quantizer (amax of the data itself, then quantize) for comparison:
+    # 5 B per element (the bf16 input read twice, the codes written once)
+    dyn_codes = [torch.empty_like(c) for c in codes]
+    dyn_desc = torch.empty((3, heads), dtype=torch.float32, device="cuda")
+    dyn_ms, _ = event_ms(torch, lambda: B.quant_dynamic([q, k, v], outs=dyn_codes,
+                                                        descale_out=dyn_desc), reps, stream)
+    dyn_bytes = 5 * (wl.q.size + wl.k.size + wl.v.size)
+    kernels["quant_dynamic_us"] = round(dyn_ms * 1e3, 2)
+    kernels["quant_dynamic_GBps"] = round(dyn_bytes / dyn_ms / 1e6, 1)
+    del dyn_codes
+    log(f"[bench] dynamic quant {dyn_ms * 1e3:.1f} us ({dyn_bytes / dyn_ms / 1e6:.0f} GB/s, "
+        f"{dyn_ms / quant_ms:.2f}x the static quantizer)")
     if chunked:
         kernels["chunked_prefill_ms"] = round(prefill_ms, 4)
         kernels["pipeline_ms"] = round(quant_ms + prefill_ms, 4)

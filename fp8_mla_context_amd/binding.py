@@ -57,6 +57,8 @@ SIGNATURES = {
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_last_error": (ctypes.c_char_p, []),
     "mla_fp8_quant_static": (ctypes.c_int, [ctypes.POINTER(QuantJob), _c_i32, _c_i32, _c_vp]),
+    "mla_fp8_quant_dynamic": (ctypes.c_int, [ctypes.POINTER(QuantJob), _c_i32, _c_i32, _c_vp,
+                                             _c_vp]),
     "mla_fp8_amax_per_head": (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp,
                                              _c_vp]),
     "mla_fp8_prefill_varlen": (ctypes.c_int, [
@@ -157,28 +159,54 @@ def amax_per_head(x, stream=None):
 def quant_static(xs: Sequence, descales: Sequence, outs: Optional[Sequence] = None, stream=None):
     """Quantize 1..3 bf16 tensors [T, H, D] (token/head strides allowed, last dim contiguous)
     with fp32 [H] descales in ONE launch. Returns uint8 E4M3 code tensors [T, H, D]."""
-    import torch
-
     if len(xs) != len(descales) or not 1 <= len(xs) <= 3:
         raise ValueError("need 1..3 tensors and one descale vector each")
+    jobs, ys, heads = _quant_jobs(xs, descales, outs)
+    _check(lib().mla_fp8_quant_static(jobs, len(xs), heads, _stream(stream)), "mla_fp8_quant_static")
+    return ys
+
+
+def _quant_jobs(xs, descales, outs):
+    import torch
+
     heads = xs[0].shape[1]
     jobs = (QuantJob * len(xs))()
     ys = []
-    for i, (x, d) in enumerate(zip(xs, descales)):
+    for i, x in enumerate(xs):
         if x.dtype != torch.bfloat16 or x.dim() != 3 or x.shape[1] != heads or \
                 (x.numel() > 0 and x.stride(2) != 1):
             raise ValueError("x must be bf16 [T, H, D] with a contiguous last dim")
-        if d.dtype != torch.float32 or d.shape != (heads,) or not d.is_contiguous():
-            raise ValueError("descale must be contiguous fp32 [H]")
+        d = None
+        if descales is not None:
+            d = descales[i]
+            if d.dtype != torch.float32 or d.shape != (heads,) or not d.is_contiguous():
+                raise ValueError("descale must be contiguous fp32 [H]")
         y = outs[i] if outs is not None else torch.empty(x.shape, dtype=torch.uint8, device=x.device)
         if y.dtype != torch.uint8 or tuple(y.shape) != tuple(x.shape) or \
                 (y.numel() > 0 and not y.is_contiguous()):
             raise ValueError("output must be contiguous uint8 with x's shape")
-        jobs[i] = QuantJob(_ptr(x), x.stride(0), x.stride(1), x.shape[0], x.shape[2], _ptr(d),
-                           _ptr(y))
+        jobs[i] = QuantJob(_ptr(x), x.stride(0), x.stride(1), x.shape[0], x.shape[2],
+                           _ptr(d) if d is not None else None, _ptr(y))
         ys.append(y)
-    _check(lib().mla_fp8_quant_static(jobs, len(xs), heads, _stream(stream)), "mla_fp8_quant_static")
-    return ys
+    return jobs, ys, heads
+
+
+def quant_dynamic(xs: Sequence, outs: Optional[Sequence] = None, descale_out=None, stream=None):
+    """Dynamic per-head quantization of 1..3 bf16 tensors [T, H, D]: descales from the
+    data's own per-head amax. Returns (codes list, fp32 descales [len(xs), H])."""
+    import torch
+
+    if not 1 <= len(xs) <= 3:
+        raise ValueError("need 1..3 tensors")
+    jobs, ys, heads = _quant_jobs(xs, None, outs)
+    if descale_out is None:
+        descale_out = torch.empty((len(xs), heads), dtype=torch.float32, device=xs[0].device)
+    if descale_out.dtype != torch.float32 or tuple(descale_out.shape) != (len(xs), heads) or \
+            not descale_out.is_contiguous():
+        raise ValueError("descale_out must be contiguous fp32 [n_tensors, H]")
+    _check(lib().mla_fp8_quant_dynamic(jobs, len(xs), heads, _ptr(descale_out), _stream(stream)),
+           "mla_fp8_quant_dynamic")
+    return ys, descale_out
 
 
 def prefill_varlen(q8, k8, v8, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,

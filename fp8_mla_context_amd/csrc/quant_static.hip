@@ -26,13 +26,14 @@ constexpr int kMaxJobs = 3;
 struct QuantJobDev {
   const uint16_t* x;
   uint8_t* y;
-  const float* descale;
+  const float* descale;  // fp32 descales, or (from_amax) the fp32 bit patterns of the amax
   int64_t stride_token;
   int64_t stride_head;
   uint32_t chunk_begin;  // first global chunk index of this job
   uint32_t n_chunks;
   int32_t head_dim;
-  int32_t vec;  // 1: 16-byte loads are aligned
+  int32_t vec;        // 1: 16-byte loads are aligned
+  int32_t from_amax;  // 1: descale = descale_of_amax(descale[h])
 };
 
 struct QuantParams {
@@ -77,6 +78,13 @@ __device__ __forceinline__ uint32_t quant_one(uint32_t xb, float d, float r) {
   return (lower + (up ? 1u : 0u)) | sign;
 }
 
+// Dynamic scales: descale = RN_fp32(amax / 448) floored at 2^-126 (1/descale stays
+// finite), or 1 when the head is all zeros (any positive descale gives the same codes).
+__device__ __forceinline__ float descale_of_amax(float amax) {
+  if (!(amax > 0.f)) return 1.f;
+  return fmaxf(__fdiv_rn(amax, 448.f), 0x1p-126f);
+}
+
 __device__ __forceinline__ uint32_t quant_pack4(uint32_t w0, uint32_t w1, float d, float r) {
   // w0 holds bf16 elements 0,1 (low, high halves), w1 elements 2,3
   uint32_t c0 = quant_one(w0 & 0xFFFFu, d, r);
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantParams
     }
     const uint32_t t = mla::fdiv(row, p.heads);
     const uint32_t h = row - t * p.heads.d;
-    const float d = jb.descale[h];
+    const float d = jb.from_amax ? descale_of_amax(jb.descale[h]) : jb.descale[h];
     const float r = 1.0f / d;
     const uint16_t* src = jb.x + static_cast<int64_t>(t) * jb.stride_token +
                           static_cast<int64_t>(h) * jb.stride_head + col * 16u;
@@ -133,56 +141,78 @@ __global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantParams
 // amax per head: max |x| over tokens and dims. Float bits of |x| order like
 // unsigned integers, so an integer atomic max is exact and order-independent.
 // NaN inputs (bits above +Inf) win the max and surface as a non-finite amax.
-
-struct AmaxParams {
-  const uint16_t* x;
-  int64_t stride_token;
-  int64_t stride_head;
-  uint32_t* amax_bits;
-  uint32_t n_rows;  // n_tokens * n_heads
-  int32_t head_dim;
-  mla::FastDiv heads;
-};
+//
+// Same 16-element chunks as the quantizer (two 16-byte loads per thread), for up
+// to three tensors in one launch; each workgroup keeps per-(tensor, head) maxima
+// in LDS and publishes them with one global atomic each at the end.
 
 __global__ __launch_bounds__(kQuantThreads) void zero_words_kernel(uint32_t* p, int n) {
   int i = blockIdx.x * kQuantThreads + threadIdx.x;
   if (i < n) p[i] = 0u;
 }
 
-// One wave per (token, head) row; lanes stride over the row's dims. Each
-// workgroup keeps its running maxima per head in LDS (n_heads <= kAmaxLdsHeads)
-// and publishes them with one global atomic per head at the end.
-constexpr int kAmaxLdsHeads = 1024;
+constexpr int kAmaxLdsSlots = 3 * 1024;  // n_jobs * n_heads maxima kept in LDS
 
-__global__ __launch_bounds__(kQuantThreads) void amax_kernel(AmaxParams p) {
-  __shared__ uint32_t smax[kAmaxLdsHeads];
+// amax_bits[j * H + h] receives the max of job j, head h (the jobs' descale field is
+// not read)
+__global__ __launch_bounds__(kQuantThreads) void amax_chunks_kernel(QuantParams p,
+                                                                    uint32_t* amax_bits) {
+  __shared__ uint32_t smax[kAmaxLdsSlots];
   const int H = static_cast<int>(p.heads.d);
-  const bool use_lds = H <= kAmaxLdsHeads;
+  const int slots = p.n_jobs * H;
+  const bool use_lds = slots <= kAmaxLdsSlots;
   if (use_lds)
-    for (int i = threadIdx.x; i < H; i += kQuantThreads) smax[i] = 0u;
+    for (int i = threadIdx.x; i < slots; i += kQuantThreads) smax[i] = 0u;
   __syncthreads();
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t waves = gridDim.x * (kQuantThreads / 64);
-  for (uint32_t row = blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6); row < p.n_rows;
-       row += waves) {
+  const uint32_t stride = gridDim.x * kQuantThreads;
+  for (uint32_t c = blockIdx.x * kQuantThreads + threadIdx.x; c < p.total_chunks; c += stride) {
+    int j = 0;
+    if (p.n_jobs > 1 && c >= p.job[1].chunk_begin) j = 1;
+    if (p.n_jobs > 2 && c >= p.job[2].chunk_begin) j = 2;
+    const QuantJobDev& jb = p.job[j];
+    const uint32_t local = c - jb.chunk_begin;
+    uint32_t row, col;
+    if (jb.head_dim == 192) {
+      row = local / 12u;
+      col = local - row * 12u;
+    } else {
+      row = local >> 3;
+      col = local & 7u;
+    }
     const uint32_t t = mla::fdiv(row, p.heads);
     const uint32_t h = row - t * p.heads.d;
-    const uint16_t* src =
-        p.x + static_cast<int64_t>(t) * p.stride_token + static_cast<int64_t>(h) * p.stride_head;
-    uint32_t m = 0;
-    for (int dd = lane; dd < p.head_dim; dd += 64) m = max(m, (uint32_t)(src[dd] & 0x7FFFu));
-    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    if (lane == 0) {
-      if (use_lds)
-        atomicMax(smax + h, m << 16);
-      else
-        atomicMax(p.amax_bits + h, m << 16);
+    const uint16_t* src = jb.x + static_cast<int64_t>(t) * jb.stride_token +
+                          static_cast<int64_t>(h) * jb.stride_head + col * 16u;
+    uint32_t w[8];
+    if (jb.vec) {
+      const uint4 a = *reinterpret_cast<const uint4*>(src);
+      const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+      w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w[i] = static_cast<uint32_t>(src[2 * i]) | (static_cast<uint32_t>(src[2 * i + 1]) << 16);
     }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    const int slot = j * H + static_cast<int>(h);
+    if (use_lds)
+      atomicMax(smax + slot, m << 16);
+    else
+      atomicMax(amax_bits + slot, m << 16);
   }
   __syncthreads();
   if (use_lds)
-    for (int i = threadIdx.x; i < H; i += kQuantThreads)
-      if (smax[i] != 0u) atomicMax(p.amax_bits + i, smax[i]);
+    for (int i = threadIdx.x; i < slots; i += kQuantThreads)
+      if (smax[i] != 0u) atomicMax(amax_bits + i, smax[i]);
+}
+
+// in place: amax bit patterns -> dynamic descales
+__global__ __launch_bounds__(kQuantThreads) void descale_of_amax_kernel(float* v, int n) {
+  int i = blockIdx.x * kQuantThreads + threadIdx.x;
+  if (i < n) v[i] = descale_of_amax(v[i]);
 }
 
 int grid_for(uint64_t work_items, int per_block) {
@@ -193,27 +223,28 @@ int grid_for(uint64_t work_items, int per_block) {
   return static_cast<int>(blocks);
 }
 
-}  // namespace
-
-extern "C" int mla_fp8_quant_static(const mla_quant_job* jobs, int32_t n_jobs, int32_t n_heads,
-                                    void* stream) {
+// Validate the jobs and fill the launch parameters. need_y: the job writes codes;
+// need_descale: the job reads caller descales. Returns MLA_OK with *total chunks.
+int build_params(const mla_quant_job* jobs, int32_t n_jobs, int32_t n_heads, bool need_y,
+                 bool need_descale, QuantParams& p, uint64_t& total) {
   if (jobs == nullptr) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "jobs is NULL");
   if (n_jobs < 1 || n_jobs > kMaxJobs)
     return mla::fail(MLA_ERR_INVALID_ARGUMENT, "n_jobs = %d not in 1..3", n_jobs);
   if (n_heads < 1) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "n_heads = %d < 1", n_heads);
-  QuantParams p{};
+  p = QuantParams{};
   p.n_jobs = n_jobs;
-  uint64_t total = 0;
+  total = 0;
   for (int j = 0; j < n_jobs; ++j) {
     const mla_quant_job& s = jobs[j];
     if (s.head_dim != 192 && s.head_dim != 128)
       return mla::fail(MLA_ERR_UNSUPPORTED, "job %d: head_dim %d is not 192 or 128", j, s.head_dim);
     if (s.n_tokens < 0) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "job %d: n_tokens < 0", j);
-    if (s.n_tokens > 0 && (s.x == nullptr || s.y == nullptr || s.descale == nullptr))
+    if (s.n_tokens > 0 && (s.x == nullptr || (need_y && s.y == nullptr) ||
+                           (need_descale && s.descale == nullptr)))
       return mla::fail(MLA_ERR_INVALID_ARGUMENT, "job %d: NULL pointer", j);
     if (s.stride_token < 0 || s.stride_head < 0)
       return mla::fail(MLA_ERR_INVALID_ARGUMENT, "job %d: negative stride", j);
-    if (s.n_tokens > 0 && !mla::aligned16(s.y))
+    if (need_y && s.n_tokens > 0 && !mla::aligned16(s.y))
       return mla::fail(MLA_ERR_INVALID_ARGUMENT, "job %d: y is not 16-byte aligned", j);
     if ((reinterpret_cast<uintptr_t>(s.x) & 1u) != 0)
       return mla::fail(MLA_ERR_INVALID_ARGUMENT, "job %d: x is not 2-byte aligned", j);
@@ -231,49 +262,80 @@ extern "C" int mla_fp8_quant_static(const mla_quant_job* jobs, int32_t n_jobs, i
     d.chunk_begin = static_cast<uint32_t>(total);
     d.n_chunks = static_cast<uint32_t>(chunks);
     d.vec = (mla::aligned16(s.x) && (s.stride_token % 8) == 0 && (s.stride_head % 8) == 0) ? 1 : 0;
+    d.from_amax = 0;
     total += chunks;
     if (total >= (1ull << 31))
       return mla::fail(MLA_ERR_UNSUPPORTED, "more than 2^35 elements in one launch");
   }
-  if (total == 0) return mla::ok();
   p.total_chunks = static_cast<uint32_t>(total);
   p.heads = mla::make_fastdiv(static_cast<uint32_t>(n_heads));
+  return MLA_OK;
+}
+
+// zero the n amax words, then the per-(job, head) maxima of the jobs' inputs
+int launch_amax(const QuantParams& p, uint64_t total, uint32_t* amax_bits, int n, hipStream_t st) {
+  hipLaunchKernelGGL(zero_words_kernel, dim3((n + kQuantThreads - 1) / kQuantThreads),
+                     dim3(kQuantThreads), 0, st, amax_bits, n);
+  int s = mla::check_launch("zero_words_kernel");
+  if (s != MLA_OK || total == 0) return s;
+  hipLaunchKernelGGL(amax_chunks_kernel, dim3(grid_for(total, kQuantThreads)), dim3(kQuantThreads),
+                     0, st, p, amax_bits);
+  return mla::check_launch("amax_chunks_kernel");
+}
+
+}  // namespace
+
+extern "C" int mla_fp8_quant_static(const mla_quant_job* jobs, int32_t n_jobs, int32_t n_heads,
+                                    void* stream) {
+  QuantParams p;
+  uint64_t total = 0;
+  const int st = build_params(jobs, n_jobs, n_heads, true, true, p, total);
+  if (st != MLA_OK) return st;
+  if (total == 0) return mla::ok();
   hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(total, kQuantThreads)),
                      dim3(kQuantThreads), 0, static_cast<hipStream_t>(stream), p);
   return mla::check_launch("quant_static_kernel");
+}
+
+extern "C" int mla_fp8_quant_dynamic(const mla_quant_job* jobs, int32_t n_jobs, int32_t n_heads,
+                                     float* descale_out, void* stream) {
+  if (descale_out == nullptr) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "descale_out is NULL");
+  QuantParams p;
+  uint64_t total = 0;
+  int st = build_params(jobs, n_jobs, n_heads, true, false, p, total);
+  if (st != MLA_OK) return st;
+  if (static_cast<int64_t>(n_jobs) * n_heads >= (1ll << 31))
+    return mla::fail(MLA_ERR_UNSUPPORTED, "n_jobs * n_heads too large");
+  const int n = n_jobs * n_heads;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(descale_out);
+  st = launch_amax(p, total, bits, n, hs);
+  if (st != MLA_OK) return st;
+  if (total > 0) {
+    for (int j = 0; j < n_jobs; ++j) {
+      p.job[j].descale = descale_out + static_cast<int64_t>(j) * n_heads;
+      p.job[j].from_amax = 1;
+    }
+    hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(total, kQuantThreads)),
+                       dim3(kQuantThreads), 0, hs, p);
+    st = mla::check_launch("quant_static_kernel");
+    if (st != MLA_OK) return st;
+  }
+  hipLaunchKernelGGL(descale_of_amax_kernel, dim3((n + kQuantThreads - 1) / kQuantThreads),
+                     dim3(kQuantThreads), 0, hs, descale_out, n);
+  return mla::check_launch("descale_of_amax_kernel");
 }
 
 extern "C" int mla_fp8_amax_per_head(const void* x, int64_t stride_token, int64_t stride_head,
                                      int64_t n_tokens, int32_t n_heads, int32_t head_dim,
                                      float* amax, void* stream) {
   if (amax == nullptr) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "amax is NULL");
-  if (n_heads < 1) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "n_heads = %d < 1", n_heads);
-  if (head_dim != 192 && head_dim != 128)
-    return mla::fail(MLA_ERR_UNSUPPORTED, "head_dim %d is not 192 or 128", head_dim);
-  if (n_tokens < 0 || stride_token < 0 || stride_head < 0)
-    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "negative size or stride");
   if (n_tokens > 0 && x == nullptr) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "x is NULL");
-  if ((reinterpret_cast<uintptr_t>(x) & 1u) != 0)
-    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "x is not 2-byte aligned");
-  const uint64_t rows = static_cast<uint64_t>(n_tokens) * static_cast<uint64_t>(n_heads);
-  if (rows >= (1ull << 31)) return mla::fail(MLA_ERR_UNSUPPORTED, "n_tokens * n_heads >= 2^31");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
-  hipLaunchKernelGGL(zero_words_kernel, dim3((n_heads + kQuantThreads - 1) / kQuantThreads),
-                     dim3(kQuantThreads), 0, st, bits, n_heads);
-  int s = mla::check_launch("zero_words_kernel");
-  if (s != MLA_OK || rows == 0) return s;
-  AmaxParams p;
-  p.x = static_cast<const uint16_t*>(x);
-  p.stride_token = stride_token;
-  p.stride_head = stride_head;
-  p.amax_bits = bits;
-  p.n_rows = static_cast<uint32_t>(rows);
-  p.head_dim = head_dim;
-  p.heads = mla::make_fastdiv(static_cast<uint32_t>(n_heads));
-  uint64_t blocks = (rows + 63) / 64;  // ~16 rows per wave
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(amax_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads), 0, st,
-                     p);
-  return mla::check_launch("amax_kernel");
+  mla_quant_job job{x, stride_token, stride_head, n_tokens, head_dim, nullptr, nullptr};
+  QuantParams p;
+  uint64_t total = 0;
+  const int st = build_params(&job, 1, n_heads, false, false, p, total);
+  if (st != MLA_OK) return st;
+  return launch_amax(p, total, reinterpret_cast<uint32_t*>(amax), n_heads,
+                     static_cast<hipStream_t>(stream));
 }

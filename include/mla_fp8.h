@@ -96,6 +96,27 @@ int mla_fp8_quant_static(const mla_quant_job* jobs, int32_t n_jobs, int32_t n_he
                          void* stream);
 
 /*
+ * Dynamic per-head quantization: the per-head amax reduction that the static
+ * path removes ("[ROCm][MLA] Add guarded gfx942 FP8 context prefill", Summary),
+ * kept as the baseline to compare with. For each job j and head h:
+ *   amax = max |x[t,h,d]| over the job's tokens and dims,
+ *   descale = RN_fp32(amax / 448) floored at 2^-126 (so 1/descale stays finite),
+ *             or 1 when the head is all zeros (any positive descale gives the same codes),
+ *   y[t,h,d] = E4M3(x[t,h,d] / descale), exactly as mla_fp8_quant_static.
+ *   jobs         as for mla_fp8_quant_static; jobs[j].descale is not read.
+ *   descale_out  device fp32 [n_jobs * n_heads], caller-owned: receives descale of
+ *                (j, h) at j * n_heads + h (usable as the descales of the prefill).
+ *                It holds the amax during the call.
+ * Inputs must be finite: a NaN or Inf element makes its head's descale non-finite and
+ * its codes unspecified (no error is raised; the device does not report back).
+ * Four launches on stream (zero, amax reduction, quantize, descale); HBM traffic
+ * 5 bytes per element (2 read twice, 1 written) against 3 for the static path.
+ * Errors as for mla_fp8_quant_static, and MLA_ERR_INVALID_ARGUMENT for a NULL descale_out.
+ */
+int mla_fp8_quant_dynamic(const mla_quant_job* jobs, int32_t n_jobs, int32_t n_heads,
+                          float* descale_out, void* stream);
+
+/*
  * Calibration: amax[h] = max |x[t,h,d]| over all tokens and dims (device fp32
  * [n_heads], overwritten). Bit-exact (max does not depend on order). The
  * pull request collects per-head maxima in a calibration pass ("What this PR

@@ -14,7 +14,9 @@ What it computes, and the passages it follows (all from the vLLM PR
                #54254, review thread on ``rmsnorm_gated_fp8_per_token``).
   quant.py     static per-head quantization with caller-supplied descales (Summary;
                "What this PR does": one-kernel static quantizer, finite positive
-               descales) and the calibration arithmetic descale = amax / 448.
+               descales), the calibration arithmetic descale = amax / 448, and the
+               dynamic variant that takes the amax of the data itself (the per-head
+               reduction the static path removes, Summary).
   attention.py softmax attention over packed variable-length sequences on the
                dequantized FP8 inputs, returning out and LSE (Background: packed
                variable-length D192/V128 kernel; "What this PR does": 12 heads,
@@ -31,7 +33,7 @@ the pages' own values.
 """
 
 from .e4m3 import decode_table, e4m3_decode, e4m3_encode  # noqa: F401
-from .quant import amax_per_head, descale_from_amax, quant_static  # noqa: F401
+from .quant import amax_per_head, descale_from_amax, quant_dynamic, quant_static  # noqa: F401
 from .attention import attention_varlen, attention_rows  # noqa: F401
 from .merge import merge_lse  # noqa: F401
 from .chunked import chunked_context, segment_plan  # noqa: F401

@@ -64,3 +64,24 @@ def descale_from_amax(amax: np.ndarray) -> np.ndarray:
     if not (np.all(np.isfinite(a)) and np.all(a > 0)):
         raise ValueError("amax must be finite and positive")
     return (a.astype(np.float64) / E4M3_MAX).astype(np.float32)
+
+
+FP32_MIN_NORMAL = 2.0 ** -126
+
+
+def quant_dynamic(x_bits: np.ndarray):
+    """Dynamic per-head quantization, the baseline the static path replaces (vLLM PR #51551,
+    Summary: the static scales remove a per-head amax reduction from every prefill step).
+
+    The amax is taken over the data being quantized: amax[h] = max |x| over its tokens and
+    dims; descale[h] = RN_fp32(amax[h] / 448), floored at 2^-126 (the smallest normal fp32,
+    so that 1/descale stays finite), or 1 for a head whose values are all zero (any positive
+    descale gives the same codes there). Inputs must be finite. Returns (codes, descale)."""
+    amax = amax_per_head(x_bits)
+    if not np.all(np.isfinite(amax)):
+        raise ValueError("dynamic quantization needs finite inputs")
+    d = np.ones(amax.shape, dtype=np.float32)
+    pos = amax > 0
+    d[pos] = (amax[pos].astype(np.float64) / E4M3_MAX).astype(np.float32)
+    d = np.maximum(d, np.float32(FP32_MIN_NORMAL)).astype(np.float32)
+    return quant_static(x_bits, d), d

@@ -136,3 +136,20 @@ def test_amax_validation_before_launch(lib):
     assert f(1 << 12, 2304, 192, 4, 12, 64, 1 << 12, None) == binding.MLA_ERR_UNSUPPORTED
     assert f(1 << 12, 2304, 192, -1, 12, 192, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
     assert f((1 << 12) + 1, 2304, 192, 4, 12, 192, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_quant_dynamic_validation_before_launch(lib):
+    f = lib.mla_fp8_quant_dynamic
+    job = binding.QuantJob(1 << 12, 192 * 12, 192, 10, 192, None, 1 << 12)  # descale not read
+    jobs = (binding.QuantJob * 3)(job, job, job)
+    assert f(jobs, 1, 12, None, None) == binding.MLA_ERR_INVALID_ARGUMENT  # no descale_out
+    assert f(None, 1, 12, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(jobs, 0, 12, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(jobs, 4, 12, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert f(jobs, 1, 0, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    bad = binding.QuantJob(1 << 12, 192 * 12, 192, 10, 64, None, 1 << 12)
+    assert f((binding.QuantJob * 1)(bad), 1, 12, 1 << 12, None) == binding.MLA_ERR_UNSUPPORTED
+    bad = binding.QuantJob(None, 192 * 12, 192, 10, 192, None, 1 << 12)
+    assert f((binding.QuantJob * 1)(bad), 1, 12, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+    bad = binding.QuantJob(1 << 12, 192 * 12, 192, 10, 192, None, (1 << 12) + 8)
+    assert f((binding.QuantJob * 1)(bad), 1, 12, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
