@@ -14,7 +14,8 @@
 //     segments of seg keys seen in full, and [off + r0, off + r1) is the
 //     diagonal (a causal call with Lq = Lk = r1 - r0); later keys are invisible;
 //   * non-causal requests split every query chunk over all key segments.
-// The host walks the plan; every step runs in the prefill and merge kernels on
+// The host walks the plan: each query chunk's parts run as ONE prefill launch over
+// all its segments (a segment table in the kernel arguments), then one merge, on
 // the caller's stream. Partials are kept in fp32 in a caller-provided
 // workspace, so the output is rounded to bf16 once, by the merge; a query
 // chunk with a single part is written straight into `out`.
@@ -131,47 +132,36 @@ extern "C" int mla_fp8_prefill_chunked(const void* q, const void* k, const void*
     if (!chunk_parts(lq, lk, seg, causal, r0, r1, parts))
       return mla::fail(MLA_ERR_INVALID_ARGUMENT, "no chunk plan");
     const int n = static_cast<int>(parts.size());
-    for (int i = 0; i < n; ++i) {
-      const Part& pt = parts[i];
-      void* o = (n == 1) ? static_cast<void*>(out8 + r0 * orow) : static_cast<void*>(ws + i * out_part);
-      float* l_;
-      int64_t lstride;
-      if (n == 1) {
-        l_ = lse ? lse + r0 : nullptr;
-        lstride = lse_stride;
-      } else {
-        l_ = reinterpret_cast<float*>(lse_ws + i * lse_part);
-        lstride = rows;
-      }
-      mla::PrefillArgs a{q8 + r0 * qrow,
-                         k8 + pt.k0 * qrow,
-                         v8 + pt.k0 * vrow,
-                         nullptr,
-                         nullptr,
-                         1,
-                         static_cast<int32_t>(rows),
-                         rows,
-                         pt.k1 - pt.k0,
-                         n_heads,
-                         descale_q,
-                         descale_k,
-                         descale_v,
-                         softmax_scale,
-                         pt.causal,
-                         o,
-                         n > 1 ? 1 : 0,
-                         l_,
-                         lstride};
+    if (n == 1) {
+      // a single part is written straight into the output rows
+      const Part& pt = parts[0];
+      mla::PrefillArgs a{q8 + r0 * qrow, k8 + pt.k0 * qrow, v8 + pt.k0 * vrow, nullptr, nullptr,
+                         1, static_cast<int32_t>(rows), rows, pt.k1 - pt.k0, n_heads, descale_q,
+                         descale_k, descale_v, softmax_scale, pt.causal, out8 + r0 * orow, 0,
+                         lse ? lse + r0 : nullptr, lse_stride};
       st = mla::prefill_launch(a, s);
       if (st != MLA_OK) return st;
-      outs[i] = o;
-      lses[i] = l_;
+      continue;
     }
-    if (n > 1) {
-      st = mla::merge_launch(n, outs, 1, lses, rows, rows, n_heads, out8 + r0 * orow,
-                             lse ? lse + r0 : nullptr, lse_stride, s);
-      if (st != MLA_OK) return st;
+    // all parts of this query chunk in ONE launch (fp32 partials in the workspace),
+    // non-causal segments first (the plan lists the causal diagonal last), then the merge
+    mla::PrefillSegment segs[kMaxParts];
+    for (int i = 0; i < n; ++i) {
+      const Part& pt = parts[i];
+      segs[i] = mla::PrefillSegment{pt.k0, static_cast<int32_t>(pt.k1 - pt.k0), pt.causal,
+                                    ws + i * out_part,
+                                    reinterpret_cast<float*>(lse_ws + i * lse_part)};
+      outs[i] = segs[i].out;
+      lses[i] = segs[i].lse;
     }
+    mla::PrefillArgs a{q8 + r0 * qrow, k8, v8, nullptr, nullptr, 1, static_cast<int32_t>(rows),
+                       rows, lk, n_heads, descale_q, descale_k, descale_v, softmax_scale, 0,
+                       nullptr, 1, nullptr, rows};
+    st = mla::prefill_launch_segments(a, segs, n, s);
+    if (st != MLA_OK) return st;
+    st = mla::merge_launch(n, outs, 1, lses, rows, rows, n_heads, out8 + r0 * orow,
+                           lse ? lse + r0 : nullptr, lse_stride, s);
+    if (st != MLA_OK) return st;
   }
   return mla::ok();
 }

@@ -71,7 +71,23 @@ struct PrefillArgs {
   float* lse;
   int64_t lse_stride;
 };
+
+// One context segment of a multi-segment launch: the same query rows attend keys
+// [k0, k0 + lk) of the launch's K/V (causal: bottom-right within the segment) and write
+// their own partial out (fp32 when the launch has out_f32) and LSE.
+constexpr int kMaxPrefillSegments = 64;
+struct PrefillSegment {
+  int64_t k0;
+  int32_t lk;
+  int32_t causal;
+  void* out;
+  float* lse;
+};
 int prefill_launch(const PrefillArgs& a, hipStream_t stream);
+// one launch over n segments for the query rows of a (a.batch == 1, no cu_seqlens; a.k/a.v
+// hold all keys, a.total_k of them; a.out, a.lse and a.causal are ignored)
+int prefill_launch_segments(const PrefillArgs& a, const PrefillSegment* segs, int n,
+                            hipStream_t stream);
 
 // LSE merge launch with validated arguments; partials are bf16 or (in_f32) fp32.
 int merge_launch(int32_t n_segments, const void* const* outs, int32_t in_f32,

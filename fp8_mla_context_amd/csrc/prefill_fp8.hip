@@ -96,6 +96,21 @@ struct PrefillParams {
   float scale_log2;
 };
 
+// Context segments of a multi-segment launch (see mla::PrefillSegment); N = 1 for the
+// ordinary launch, whose table is unused.
+struct SegDev {
+  int64_t k0;
+  int32_t lk;
+  int32_t causal;
+  void* out;
+  float* lse;
+};
+template <int N>
+struct SegTable {
+  int32_t n;
+  SegDev e[N];
+};
+
 __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
   // cbsz = blgp = 0: both operands E4M3; zero scales select the unscaled instruction
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -191,7 +206,9 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-__global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(PrefillParams p) {
+template <int kNSeg>
+__global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(PrefillParams p,
+                                                                        SegTable<kNSeg> st) {
   // three K/V tile buffers: tile t is in buffer t % 3
   __shared__ __attribute__((aligned(16))) uint8_t lds[3 * (kKTile + kVTile)];
 
@@ -200,8 +217,26 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int H = p.n_heads;
 
-  int h, b, m_tile;
-  if (p.xcd_order) {
+  int h, b = 0, m_tile;
+  int64_t q0 = 0, q1 = p.total_q, k0 = 0, k1 = p.total_k;
+  bool causal = p.causal != 0;
+  void* out_ptr = p.out;
+  float* lse_ptr = p.lse;
+  if constexpr (kNSeg > 1) {
+    // multi-segment launch: segments in the host's order (heaviest first), then query
+    // tiles from the last, heads fastest
+    int idx = blockIdx.x;
+    h = idx % H;
+    idx /= H;
+    m_tile = p.n_m_tiles - 1 - idx % p.n_m_tiles;
+    const int e = idx / p.n_m_tiles;
+    const SegDev& sg = st.e[e];
+    k0 = min(max(sg.k0, (int64_t)0), p.total_k);
+    k1 = min(k0 + sg.lk, p.total_k);
+    causal = sg.causal != 0;
+    out_ptr = sg.out;
+    lse_ptr = sg.lse;
+  } else if (p.xcd_order) {
     // One sequence: workgroups are dealt round-robin to the 8 XCDs (block % 8). Each
     // head's query tiles are split into an even and an odd half (equal causal work) and
     // each XCD takes H/4 consecutive half-heads, heaviest tile first, so its L2 serves
@@ -213,7 +248,6 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     const int half = hp * xcd + slot % hp;  // 0 .. 2H-1
     const int rank = slot / hp;             // 0 .. n_m/2 - 1
     h = half >> 1;
-    b = 0;
     m_tile = p.n_m_tiles - 2 + (half & 1) - 2 * rank;
   } else {
     // heaviest query tiles first; heads, then sequences, vary fastest
@@ -226,8 +260,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   }
 
   // packed sequences from cu_seqlens, or one sequence spanning all tokens
-  int64_t q0 = 0, q1 = p.total_q, k0 = 0, k1 = p.total_k;
-  if (p.cu_q != nullptr) {
+  if (kNSeg == 1 && p.cu_q != nullptr) {
     q0 = p.cu_q[b];
     q1 = p.cu_q[b + 1];
     k0 = p.cu_k[b];
@@ -242,7 +275,6 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   const int row0 = m_tile * kBM;
   if (row0 >= Lq) return;  // uniform over the workgroup
   const int off = Lk - Lq;
-  const bool causal = p.causal != 0;
   int kend = Lk;
   if (causal) kend = min(Lk, max(0, min(Lq, row0 + kBM) + off));
   const int n_tiles = (kend + kBN - 1) / kBN;
@@ -581,7 +613,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     const float inv = (l_tot > 0.f) ? p.dv[h] / (256.f * l_tot) : 0.f;
     const int64_t obase = (q0 + my_row) * (static_cast<int64_t>(H) * kDv) + h * kDv;
     if (p.out_f32) {
-      float* op = static_cast<float*>(p.out) + obase;
+      float* op = static_cast<float*>(out_ptr) + obase;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -590,7 +622,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
               make_float4(o[db][4 * grp4 + 0] * inv, o[db][4 * grp4 + 1] * inv,
                           o[db][4 * grp4 + 2] * inv, o[db][4 * grp4 + 3] * inv);
     } else {
-      uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
+      uint16_t* op = static_cast<uint16_t*>(out_ptr) + obase;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -603,8 +635,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
               make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
         }
     }
-    if (g == 0 && p.lse != nullptr)
-      p.lse[static_cast<int64_t>(h) * p.lse_stride + q0 + my_row] =
+    if (g == 0 && lse_ptr != nullptr)
+      lse_ptr[static_cast<int64_t>(h) * p.lse_stride + q0 + my_row] =
           (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
@@ -613,14 +645,14 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
 
 namespace mla {
 
-int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
-  if (a.total_q == 0 || a.batch == 0 || a.max_seqlen_q == 0) return ok();
+namespace {
+
+// common checks and parameters of both launch forms; returns the number of query tiles
+int prefill_params(const PrefillArgs& a, PrefillParams& prm, int64_t& n_m) {
   if (a.total_k * static_cast<int64_t>(a.n_heads) * kDqk >= (1ll << 31))
     return fail(MLA_ERR_UNSUPPORTED, "total_k * n_heads * 192 must be < 2^31");
-  const int64_t n_m = (static_cast<int64_t>(a.max_seqlen_q) + kBM - 1) / kBM;
-  const int64_t blocks = n_m * a.batch * a.n_heads;
-  if (blocks >= (1ll << 31)) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
-  PrefillParams prm;
+  n_m = (static_cast<int64_t>(a.max_seqlen_q) + kBM - 1) / kBM;
+  prm = PrefillParams{};
   prm.q = static_cast<const uint8_t*>(a.q);
   prm.k = static_cast<const uint8_t*>(a.k);
   prm.v = static_cast<const uint8_t*>(a.v);
@@ -640,9 +672,48 @@ int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   prm.n_m_tiles = static_cast<int32_t>(n_m);
   prm.causal = a.causal;
   prm.scale_log2 = a.softmax_scale * 1.44269504088896340736f;
+  return MLA_OK;
+}
+
+}  // namespace
+
+int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
+  if (a.total_q == 0 || a.batch == 0 || a.max_seqlen_q == 0) return ok();
+  PrefillParams prm;
+  int64_t n_m = 0;
+  const int st = prefill_params(a, prm, n_m);
+  if (st != MLA_OK) return st;
+  const int64_t blocks = n_m * a.batch * a.n_heads;
+  if (blocks >= (1ll << 31)) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
   prm.xcd_order = (a.batch == 1 && a.n_heads % 4 == 0 && n_m % 2 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(prefill_fp8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                     stream, prm);
+  SegTable<1> none{};
+  hipLaunchKernelGGL(prefill_fp8_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                     0, stream, prm, none);
+  return check_launch("prefill_fp8_kernel");
+}
+
+int prefill_launch_segments(const PrefillArgs& a, const PrefillSegment* segs, int n,
+                            hipStream_t stream) {
+  if (n < 1 || n > kMaxPrefillSegments)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%d segments not in 1..%d", n, kMaxPrefillSegments);
+  if (a.batch != 1 || a.cu_q != nullptr)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "segments need one sequence without cu_seqlens");
+  if (a.total_q == 0 || a.max_seqlen_q == 0) return ok();
+  PrefillParams prm;
+  int64_t n_m = 0;
+  const int st = prefill_params(a, prm, n_m);
+  if (st != MLA_OK) return st;
+  SegTable<kMaxPrefillSegments> tab{};
+  tab.n = n;
+  for (int i = 0; i < n; ++i) {
+    if (segs[i].k0 < 0 || segs[i].lk < 0 || segs[i].k0 + segs[i].lk > a.total_k)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "segment %d outside the keys", i);
+    tab.e[i] = SegDev{segs[i].k0, segs[i].lk, segs[i].causal, segs[i].out, segs[i].lse};
+  }
+  const int64_t blocks = n_m * n * a.n_heads;
+  if (blocks >= (1ll << 31)) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
+  hipLaunchKernelGGL(prefill_fp8_kernel<kMaxPrefillSegments>, dim3(static_cast<unsigned>(blocks)),
+                     dim3(kThreads), 0, stream, prm, tab);
   return check_launch("prefill_fp8_kernel");
 }
 
