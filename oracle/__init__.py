@@ -20,7 +20,8 @@ What it computes, and the passages it follows (all from the vLLM PR
   attention.py softmax attention over packed variable-length sequences on the
                dequantized FP8 inputs, returning out and LSE (Background: packed
                variable-length D192/V128 kernel; "What this PR does": 12 heads,
-               D192 Q/K, D128 V).
+               D192 Q/K, D128 V); the same definition on bf16 inputs is the BF16
+               comparator of the close comment.
   merge.py     log-sum-exp merge of per-segment partials ("What this PR does": Q is
                quantized once and reused across context segments).
   chunked.py   segmented drivers: each context segment is attended separately and
@@ -34,6 +35,7 @@ the pages' own values.
 
 from .e4m3 import decode_table, e4m3_decode, e4m3_encode  # noqa: F401
 from .quant import amax_per_head, descale_from_amax, quant_dynamic, quant_static  # noqa: F401
-from .attention import attention_varlen, attention_rows  # noqa: F401
+from .attention import (attention_rows, attention_rows_bf16, attention_varlen,  # noqa: F401
+                        attention_varlen_bf16)
 from .merge import merge_lse  # noqa: F401
 from .chunked import chunked_context, segment_plan  # noqa: F401
