@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "causal TFLOP/s + % FP8 MFMA peak, MLA D192/V128 12-head varlen prefill"
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, published (at 2.4 GHz)
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA, published
 PEAK_CLOCK_GHZ = 2.4
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 FLOP_PER_PAIR = 2 * (192 + 128)
@@ -265,6 +266,27 @@ def main(argv=None):
             f"{rows} rows: {merge_ms * 1e3:.1f} us ({merge_bytes / merge_ms / 1e6:.0f} GB/s)")
     else:
         kernels["prefill_ms"] = round(prefill_ms, 4)
+
+    # the BF16 comparator: the same attention on the unquantized bf16 Q/K/V, one launch
+    # (unsegmented for the chunked workloads), against the FP8 path of this step
+    out16 = torch.empty_like(out)
+    lse16 = torch.empty_like(lse)
+    bf16_ms, _ = event_ms(torch, lambda: B.prefill_varlen_bf16(
+        q, k, v, cu_q, cu_k, wl.max_seqlen_q, wl.max_seqlen_k, wl.softmax_scale, wl.causal,
+        out=out16, lse=lse16), reps, stream)
+    del out16, lse16
+    bf16_tf = flop / (bf16_ms * 1e-3) / 1e12
+    kernels["bf16_comparator"] = {
+        "prefill_ms": round(bf16_ms, 4),
+        "TFLOPs": round(bf16_tf, 2),
+        "frac_bf16_peak": round(bf16_tf / BF16_PEAK_TFLOPS, 4),
+        "fp8_prefill_speedup": round(bf16_ms / prefill_ms, 3),
+        "fp8_pipeline_speedup": round(bf16_ms / (quant_ms + prefill_ms), 3),
+    }
+    log(f"[bench] bf16 comparator: {bf16_ms:.3f} ms = {bf16_tf:.1f} TFLOP/s "
+        f"({100 * bf16_tf / BF16_PEAK_TFLOPS:.1f}% of bf16 peak); FP8 {what} is "
+        f"{bf16_ms / prefill_ms:.2f}x, quant + {what} {bf16_ms / (quant_ms + prefill_ms):.2f}x "
+        f"as fast")
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20)

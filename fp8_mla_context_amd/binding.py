@@ -64,6 +64,9 @@ SIGNATURES = {
     "mla_fp8_prefill_varlen": (ctypes.c_int, [
         _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32,
         _c_i32, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "mla_bf16_prefill_varlen": (ctypes.c_int, [
+        _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32,
+        _c_i32, ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_i64, _c_vp]),
     "mla_merge_lse": (ctypes.c_int, [
         _c_i32, ctypes.POINTER(_c_vp), ctypes.POINTER(_c_vp), _c_i64, _c_i64, _c_i32, _c_i32, _c_vp,
         _c_vp, _c_i64, _c_vp]),
@@ -237,6 +240,37 @@ def prefill_varlen(q8, k8, v8, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, ma
         int(max_seqlen_q), int(max_seqlen_k), tq, tk, heads, q8.shape[2], v8.shape[2],
         _ptr(descale_q), _ptr(descale_k), _ptr(descale_v), float(softmax_scale), int(bool(causal)),
         _ptr(out), _ptr(lse), int(lse_stride), _stream(stream)), "mla_fp8_prefill_varlen")
+    return out, lse
+
+
+def prefill_varlen_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                        softmax_scale: float, causal: bool, out=None, lse=None,
+                        lse_stride: Optional[int] = None, stream=None):
+    """BF16 varlen attention (the comparator). q [Tq,H,192], k [Tk,H,192], v [Tk,H,128] bf16
+    (contiguous). Returns (out bf16 [Tq,H,128], lse fp32 [H, lse_stride])."""
+    import torch
+
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError("q/k/v must be contiguous bf16 [T, H, D]")
+    for t in (cu_seqlens_q, cu_seqlens_k):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous int32")
+    tq, heads = q.shape[0], q.shape[1]
+    tk = k.shape[0]
+    if out is None:
+        out = torch.empty((tq, heads, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse_stride = tq if lse_stride is None else lse_stride
+        lse = torch.empty((heads, lse_stride), dtype=torch.float32, device=q.device)
+    elif lse_stride is None:
+        lse_stride = lse.stride(0)
+    batch = cu_seqlens_q.shape[0] - 1
+    _check(lib().mla_bf16_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
+        int(max_seqlen_q), int(max_seqlen_k), tq, tk, heads, q.shape[2], v.shape[2],
+        float(softmax_scale), int(bool(causal)), _ptr(out), _ptr(lse), int(lse_stride),
+        _stream(stream)), "mla_bf16_prefill_varlen")
     return out, lse
 
 

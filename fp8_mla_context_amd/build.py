@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmla_fp8.so")
 
-SOURCES = ["abi.hip", "quant_static.hip", "merge_lse.hip", "prefill_fp8.hip", "chunked.hip"]
+SOURCES = ["abi.hip", "quant_static.hip", "merge_lse.hip", "prefill_fp8.hip", "prefill_bf16.hip",
+           "chunked.hip"]
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
 HIP_FLAGS = [

@@ -165,6 +165,28 @@ int mla_fp8_prefill_varlen(const void* q, const void* k, const void* v,
                            const float* descale_v, float softmax_scale, int32_t causal,
                            void* out, float* lse, int64_t lse_stride, void* stream);
 
+/*
+ * BF16 comparator: the same attention on bf16 Q/K/V, with no quantization and no
+ * scales. The close comment of the pull request measures the FP8 kernel against
+ * the BF16 attention that already covers D192/V128 (faster on the non-causal
+ * chunk shape, slower on both causal shapes); this is that comparison's other side,
+ * on the same MFMA blocking as mla_fp8_prefill_varlen.
+ *
+ *   q, k, v       device bf16, contiguous [total_q, n_heads, 192], [total_k, n_heads, 192],
+ *                 [total_k, n_heads, 128]; 16-byte aligned; finite values
+ *   cu_seqlens_q/k, batch, max_seqlen_q/k, total_q/k, n_heads, head dims, softmax_scale,
+ *   causal, out, lse, lse_stride, stream: as for mla_fp8_prefill_varlen (logits are
+ *                 softmax_scale * <q_i, k_j> of the bf16 values).
+ *   Errors as for mla_fp8_prefill_varlen.
+ */
+int mla_bf16_prefill_varlen(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int64_t total_q, int64_t total_k, int32_t n_heads,
+                            int32_t head_dim_qk, int32_t head_dim_v, float softmax_scale,
+                            int32_t causal, void* out, float* lse, int64_t lse_stride,
+                            void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* LSE merge across context segments                                         */
 /* ------------------------------------------------------------------------ */

@@ -97,6 +97,29 @@ def test_prefill_validation_before_launch(lib):
     assert _prefill(lib, max_q=0) == binding.MLA_OK
 
 
+def _prefill_bf16(lib, **kw):
+    args = dict(q=1 << 12, k=1 << 12, v=1 << 12, cu_q=1 << 12, cu_k=1 << 12, batch=1,
+                max_q=128, max_k=128, total_q=128, total_k=128, heads=12, dqk=192, dv_=128,
+                scale=0.07, causal=1, out=1 << 12, lse=None, lse_stride=128, stream=None)
+    args.update(kw)
+    return lib.mla_bf16_prefill_varlen(*args.values())
+
+
+def test_prefill_bf16_validation_before_launch(lib):
+    assert _prefill_bf16(lib, dqk=128) == binding.MLA_ERR_UNSUPPORTED
+    assert _prefill_bf16(lib, dv_=192) == binding.MLA_ERR_UNSUPPORTED
+    assert _prefill_bf16(lib, heads=0) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill_bf16(lib, causal=-1) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill_bf16(lib, scale=-0.5) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill_bf16(lib, k=None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill_bf16(lib, cu_k=None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill_bf16(lib, v=(1 << 12) + 2) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill_bf16(lib, lse=1 << 12, lse_stride=127) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert _prefill_bf16(lib, total_k=1 << 31) == binding.MLA_ERR_UNSUPPORTED
+    assert _prefill_bf16(lib, total_q=0, q=None, out=None) == binding.MLA_OK
+    assert _prefill_bf16(lib, batch=0) == binding.MLA_OK
+
+
 def test_quant_validation_before_launch(lib):
     job = binding.QuantJob(1 << 12, 192 * 12, 192, 10, 192, 1 << 12, 1 << 12)
     jobs = (binding.QuantJob * 3)(job, job, job)
