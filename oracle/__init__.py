@@ -26,6 +26,10 @@ What it computes, and the passages it follows (all from the vLLM PR
                quantized once and reused across context segments).
   chunked.py   segmented drivers: each context segment is attended separately and
                the partials merged; must equal the unsegmented result.
+  producer.py  the un-absorbed MLA keys and values expanded from the latent cache per
+               head (bf16 projection, rope part shared by the heads), then quantized
+               (vLLM PR "[ROCm][Kimi-K3] Fold q_b_proj and W_UK for MLA decode",
+               #60110, Purpose: prefill keeps the un-absorbed form; its shapes).
 
 Parity pins: every function is checked by tests under ``tests/test_oracle_*.py``
 against closed forms, exhaustive exact-rational rounding, brute force on tiny
@@ -39,3 +43,4 @@ from .attention import (attention_rows, attention_rows_bf16, attention_varlen,  
                         attention_varlen_bf16)
 from .merge import merge_lse  # noqa: F401
 from .chunked import chunked_context, segment_plan  # noqa: F401
+from .producer import kv_produce, kv_project_bf16, rn_bf16_bits  # noqa: F401
