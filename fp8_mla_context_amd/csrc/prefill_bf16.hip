@@ -61,6 +61,11 @@ constexpr int kVRegion = kVInstr * 1024;
 constexpr int kStage = kKRegion + kVRegion;            // 21504 bytes
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;
+#ifndef MLA_BF16_AHEAD
+#define MLA_BF16_AHEAD 3
+#endif
+constexpr int kAhead = MLA_BF16_AHEAD;  // LDS operand prefetch distance, in MFMAs
+static_assert(kAhead >= 1 && kAhead <= 4, "prefetch distance");
 static_assert(kBN * kKSlots <= kKInstr * 64, "K tile slots");
 static_assert(2 * 3 * kStage <= 160 * 1024, "two workgroups per CU");
 
@@ -300,10 +305,15 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_bf16_kernel(Bf16Pa
     const bool active = it < wave_iters;
     const uint8_t* kl = kbuf(it + 1);
     const uint8_t* vl = kbuf(it > 0 ? it - 1 : 0) + kKRegion;
-    v8bf va, ka;
+    // operands are read kAhead MFMAs of their kind ahead of use (a ring of kAhead
+    // registers each): a bf16 MFMA is too short to cover an LDS read issued just before it
+    v8bf va[kAhead], ka[kAhead];
     if (active) {
-      va = vt_operand(vl, 0, 0);
-      ka = k_operand(kl, 0);
+#pragma unroll
+      for (int j = 0; j < kAhead; ++j) {
+        va[j] = vt_operand(vl, j & 3, j >> 2);
+        ka[j] = k_operand(kl, j);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     int issued = 0;
@@ -351,19 +361,19 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_bf16_kernel(Bf16Pa
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int db = j & 3, ck = j >> 2;
-        o[db] = mfma_bf16(va, pb_prev[ck], o[db]);
-        if (j < 7) va = vt_operand(vl, (j + 1) & 3, (j + 1) >> 2);
+        o[db] = mfma_bf16(va[j % kAhead], pb_prev[ck], o[db]);
+        if (j + kAhead < 8) va[j % kAhead] = vt_operand(vl, (j + kAhead) & 3, (j + kAhead) >> 2);
         __builtin_amdgcn_sched_barrier(0);
-        s_n = mfma_bf16(ka, qf[j], s_n);
-        ka = k_operand(kl, j + 1);
+        s_n = mfma_bf16(ka[j % kAhead], qf[j], s_n);
+        ka[j % kAhead] = k_operand(kl, j + kAhead);
         if (j == 3) pb_cur[0] = softmax_chunk(s_c, nbias, 0);
         if (j == 7) pb_cur[1] = softmax_chunk(s_c, nbias, 1);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int kb = 8; kb < 12; ++kb) {
-        s_n = mfma_bf16(ka, qf[kb], s_n);
-        if (kb < 11) ka = k_operand(kl, kb + 1);
+        s_n = mfma_bf16(ka[kb % kAhead], qf[kb], s_n);
+        if (kb + kAhead < 12) ka[kb % kAhead] = k_operand(kl, kb + kAhead);
       }
       asm volatile("" ::"v"(pb_cur[0]), "v"(pb_cur[1]), "v"(l_run));
 
