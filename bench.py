@@ -288,6 +288,29 @@ def main(argv=None):
         f"{bf16_ms / prefill_ms:.2f}x, quant + {what} {bf16_ms / (quant_ms + prefill_ms):.2f}x "
         f"as fast")
 
+    # the un-absorbed K/V producer fused with the static quantizer, for this workload's keys
+    from synth import make_latent
+
+    cache_bits, w_bits = make_latent(7, wl.total_k, heads)
+    d_cache, d_w = dev_bf16(cache_bits), dev_bf16(w_bits)
+    del cache_bits, w_bits
+    pk8 = torch.empty((wl.total_k, heads, 192), dtype=torch.uint8, device="cuda")
+    pv8 = torch.empty((wl.total_k, heads, 128), dtype=torch.uint8, device="cuda")
+    prod_ms, _ = event_ms(torch, lambda: B.kv_produce(
+        d_cache[:, :512], d_cache[:, 512:], d_w, descales[1], descales[2], k8=pk8, v8=pv8),
+        reps, stream)
+    prod_bytes = wl.total_k * (576 * 2 + heads * 320) + d_w.numel() * 2
+    prod_flop = 2.0 * wl.total_k * heads * 256 * 512
+    kernels["kv_produce"] = {
+        "tokens": wl.total_k, "us": round(prod_ms * 1e3, 2),
+        "TFLOPs": round(prod_flop / (prod_ms * 1e-3) / 1e12, 1),
+        "frac_bf16_peak": round(prod_flop / (prod_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "GBps": round(prod_bytes / prod_ms / 1e6, 1), "bytes": prod_bytes,
+    }
+    del d_cache, d_w, pk8, pv8
+    log(f"[bench] kv producer ({wl.total_k} tokens): {prod_ms * 1e3:.1f} us, "
+        f"{prod_flop / (prod_ms * 1e-3) / 1e12:.0f} TFLOP/s, {prod_bytes / prod_ms / 1e6:.0f} GB/s")
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)

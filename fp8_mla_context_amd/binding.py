@@ -61,6 +61,9 @@ SIGNATURES = {
                                              _c_vp]),
     "mla_fp8_amax_per_head": (ctypes.c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp,
                                              _c_vp]),
+    "mla_fp8_kv_produce": (ctypes.c_int, [
+        _c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
+        _c_vp, _c_vp, _c_vp, _c_vp]),
     "mla_fp8_prefill_varlen": (ctypes.c_int, [
         _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32,
         _c_i32, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_i64, _c_vp]),
@@ -210,6 +213,38 @@ def quant_dynamic(xs: Sequence, outs: Optional[Sequence] = None, descale_out=Non
     _check(lib().mla_fp8_quant_dynamic(jobs, len(xs), heads, _ptr(descale_out), _stream(stream)),
            "mla_fp8_quant_dynamic")
     return ys, descale_out
+
+
+def kv_produce(c_kv, k_pe, w_kv_b, descale_k, descale_v, out_bf16: bool = False, k8=None,
+               v8=None, stream=None):
+    """Un-absorbed K/V expansion + static quantization. c_kv [T, >=512] and k_pe [T, >=64] bf16
+    (row-strided views allowed), w_kv_b bf16 [H*256, 512]. Returns (k8 [T,H,192], v8 [T,H,128]
+    uint8 codes) and, with out_bf16, also the bf16 K and V."""
+    import torch
+
+    for t in (c_kv, k_pe, w_kv_b):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("c_kv, k_pe and w_kv_b must be bf16 [rows, cols] with unit column stride")
+    n = c_kv.shape[0]
+    if k_pe.shape[0] != n:
+        raise ValueError("c_kv and k_pe must have the same number of rows")
+    heads = w_kv_b.shape[0] // 256
+    if w_kv_b.shape[0] != heads * 256 or not w_kv_b.is_contiguous():
+        raise ValueError("w_kv_b must be contiguous [n_heads * 256, 512]")
+    dev = c_kv.device
+    if k8 is None:
+        k8 = torch.empty((n, heads, 192), dtype=torch.uint8, device=dev)
+    if v8 is None:
+        v8 = torch.empty((n, heads, D_V), dtype=torch.uint8, device=dev)
+    kb = vb = None
+    if out_bf16:
+        kb = torch.empty((n, heads, 192), dtype=torch.bfloat16, device=dev)
+        vb = torch.empty((n, heads, D_V), dtype=torch.bfloat16, device=dev)
+    _check(lib().mla_fp8_kv_produce(
+        _ptr(c_kv), c_kv.stride(0), _ptr(k_pe), k_pe.stride(0), _ptr(w_kv_b), n, heads,
+        w_kv_b.shape[1], k_pe.shape[1], _ptr(descale_k), _ptr(descale_v), _ptr(k8), _ptr(v8),
+        _ptr(kb), _ptr(vb), _stream(stream)), "mla_fp8_kv_produce")
+    return (k8, v8, kb, vb) if out_bf16 else (k8, v8)
 
 
 def prefill_varlen(q8, k8, v8, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,

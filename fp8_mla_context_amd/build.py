@@ -19,7 +19,7 @@ LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmla_fp8.so")
 
 SOURCES = ["abi.hip", "quant_static.hip", "merge_lse.hip", "prefill_fp8.hip", "prefill_bf16.hip",
-           "chunked.hip"]
+           "chunked.hip", "kv_producer.hip"]
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
 HIP_FLAGS = [

@@ -1,0 +1,300 @@
+// Un-absorbed MLA K/V producer fused with the static per-head FP8 quantizer (gfx950).
+//
+// "[ROCm][Kimi-K3] Fold q_b_proj and W_UK for MLA decode" (vLLM #60110), Purpose:
+// prefill keeps the un-absorbed form, so keys and values are expanded from the latent
+// cache per head; the page gives latent rank 512, 192-wide key heads of which 64 dims
+// are the rope part, and 12 heads per rank. The quantizer is the static per-head one of
+// "[ROCm][MLA] Add guarded gfx942 FP8 context prefill" (#51551), Summary.
+//
+// For token t and head h, with latent row c_t (512 bf16) and rope key p_t (64 bf16):
+//   K[t, h] = [ RN_bf16(W_UK[h] c_t) | p_t ],  V[t, h] = RN_bf16(W_UV[h] c_t)
+//   k8 = E4M3(K / dk[h]),  v8 = E4M3(V / dv[h])   (exact quotient, nearest even)
+// W is [H * 256, 512] bf16: rows 256 h .. 256 h + 127 are W_UK[h], the next 128 W_UV[h].
+//
+// Design:
+//  * One workgroup = 8 waves = 128 tokens x one head's 256 output features. Y^T = W_h C^T
+//    on v_mfma_f32_32x32x16_bf16 with weight rows as the A operand and latent rows as
+//    the B operand, so a lane's accumulator holds one token and 4 x 4 consecutive
+//    features. Wave w owns tokens 64 (w & 1) .. + 63 and features 64 (w >> 1) .. + 63.
+//    Work items (token tile, head) are dealt to the XCDs in contiguous ranges, so the
+//    twelve workgroups of a token tile share its latent rows in one L2 and the 3 MB
+//    weight stays resident in each XCD's L2.
+//  * The 512-deep reduction runs in 16 chunks of 32; chunk c's weight rows (256 x 64 B)
+//    and latent rows (128 x 64 B) are DMA'd (global_load_lds_dwordx4) into LDS buffer
+//    c % 2, rows padded to 80 bytes (the 16-byte operand reads of 16 consecutive rows hit
+//    distinct banks), one chunk ahead of their use. Two workgroups share a CU.
+//  * Epilogue: fp32 -> bf16 (v_cvt_pk_bf16_f32, nearest even) -> E4M3 code (the exact
+//    quantizer of the standalone kernel; it dominates the kernel's VALU time). The codes
+//    pass through LDS so that each thread stores whole 16-byte pieces of k8 / v8 rows;
+//    the rope part is quantized with the head's key scale, 16 values per thread. The
+//    bf16 K and V can be written as well (for a BF16 attention path).
+#include "device_common.h"
+#include "e4m3_quant.h"
+#include "mla_internal.h"
+
+namespace {
+
+using namespace mla::dev;
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kNope = 128;
+constexpr int kDv = 128;
+constexpr int kFeat = kNope + kDv;  // 256 output features per head
+constexpr int kThreads = 512;       // 8 waves
+constexpr int kTM = 128;            // tokens per workgroup
+constexpr int kKC = 32;             // reduction chunk
+constexpr int kNChunks = kLatent / kKC;
+constexpr int kRowBytes = 80;       // 64 data bytes + 16 pad per LDS row
+constexpr int kWRegion = kFeat * kRowBytes;  // 20480
+constexpr int kCRegion = kTM * kRowBytes;    // 10240
+constexpr int kStage = kWRegion + kCRegion;  // 30720
+// Two LDS buffers (60 KB) leave room for two workgroups per CU, so that one workgroup's
+// quantizing epilogue overlaps the other's projection; a chunk is loaded one chunk ahead.
+constexpr int kStages = 2;
+constexpr int kWgPerCu = 2;
+constexpr int kWInstr = kFeat * 5 / 64;  // 20 DMA instructions (5 slots per row)
+constexpr int kCInstr = kTM * 5 / 64;    // 10
+constexpr int kInstr = kWInstr + kCInstr;
+constexpr int kPerWave = (kInstr + 7) / 8;  // 4
+constexpr int kCodeStride = kFeat + 16;  // LDS bytes per token row of the code tile
+static_assert(kStages * kStage >= kTM * kCodeStride, "the code tile reuses the stage buffers");
+
+struct ProducerParams {
+  const uint16_t* c_kv;
+  const uint16_t* k_pe;
+  const uint16_t* w;
+  const float* dk;
+  const float* dv;
+  uint8_t* k8;
+  uint8_t* v8;
+  uint16_t* kb;  // optional bf16 K [T, H, 192]
+  uint16_t* vb;  // optional bf16 V [T, H, 128]
+  int64_t c_stride;   // elements between latent rows
+  int64_t pe_stride;  // elements between rope rows
+  int64_t n_tokens;
+  int32_t n_heads;
+  int32_t xcd_order;  // 1: the grid size is a multiple of 8 (see the block mapping)
+};
+
+__device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(ProducerParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = p.n_heads;
+  // Work item v = (tile, head), heads fastest. With xcd_order, workgroup b (dealt to XCD
+  // b % 8) takes v = (b % 8) * (blocks / 8) + b / 8: each XCD gets a contiguous range, so
+  // the twelve heads of a token tile read its latent rows through one L2, and W stays
+  // resident there.
+  const int nb = gridDim.x;
+  const int v = p.xcd_order ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int h = v % H;
+  const int64_t t0 = static_cast<int64_t>(v / H) * kTM;
+  const int n_tok = static_cast<int>(min<int64_t>(kTM, p.n_tokens - t0));  // >= 1
+
+  // DMA slots: instruction i (i = wave + 8 j) writes 16-byte LDS slots 64 i + lane of the
+  // stage; slots 0..1279 are weight rows (5 per row: 4 data + 1 pad that repeats the last
+  // piece), then 640 slots of latent rows (rows past the last token repeat it).
+  const uint8_t* w_base = reinterpret_cast<const uint8_t*>(p.w) +
+                          static_cast<int64_t>(h) * kFeat * kLatent * 2;
+  const uint8_t* c_base = reinterpret_cast<const uint8_t*>(p.c_kv) + t0 * p.c_stride * 2;
+  uint32_t dma_off[kPerWave];
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int i = min(wave + 8 * j, kInstr - 1);
+    const int s = (i < kWInstr ? i * 64 : (i - kWInstr) * 64) + lane;
+    const int row = s / 5;
+    const int piece = min(s - 5 * row, 3);
+    if (i < kWInstr)
+      dma_off[j] = static_cast<uint32_t>(row * kLatent * 2 + 16 * piece);
+    else
+      dma_off[j] = static_cast<uint32_t>(min(row, n_tok - 1) * p.c_stride * 2 + 16 * piece);
+  }
+  auto issue = [&](int c) {
+    uint8_t* stage = lds + (c % kStages) * kStage;
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int i = wave + 8 * j;  // wave-uniform
+      if (i < kInstr) {
+        const uint8_t* base = uniform_ptr((i < kWInstr ? w_base : c_base) + c * kKC * 2);
+        const uint32_t dst =
+            lds_address(stage) + (i < kWInstr ? 1024u * i : kWRegion + 1024u * (i - kWInstr));
+        dma_load16(base, dma_off[j], dst);
+      }
+    }
+  };
+  const int n_mine = (kInstr - wave + 7) / 8;  // DMA instructions of this wave per chunk
+
+  const int g = lane >> 5, col = lane & 31;
+  const int tq = wave & 1, fq = wave >> 1;
+  v16f acc[2][2];
+#pragma unroll
+  for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[fb][tb][r] = 0.f;
+
+  // The rope part, K[t, h, 128 + i] = E4M3(p_t[i] / dk[h]): 16 values per thread, loaded
+  // here (older than the first chunks' loads, so the waits below cover them) and
+  // quantized in the epilogue.
+  const int pe_tok = tid >> 2, pe_pc = tid & 3;
+  uint4 pe_a = make_uint4(0, 0, 0, 0), pe_b = pe_a;
+  if (pe_tok < n_tok) {
+    const uint16_t* src = p.k_pe + (t0 + pe_tok) * p.pe_stride + 16 * pe_pc;
+    pe_a = *reinterpret_cast<const uint4*>(src);
+    pe_b = *reinterpret_cast<const uint4*>(src + 8);
+  }
+  // chunks [0, next) have been issued; before the barrier that ends iteration c, chunk
+  // c + 1 must have landed, so the loads of chunks c + 2 .. next - 1 may stay in flight
+  int next = 0;
+  for (; next < kStages - 1; ++next) issue(next);
+  wait_vmcnt(n_mine * (next - 1));
+  block_barrier();
+  for (int c = 0; c < kNChunks; ++c) {
+    if (next < kNChunks) issue(next++);
+    const uint8_t* stage = lds + (c % kStages) * kStage;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v8bf a[2], b[2];
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+        a[fb] = *reinterpret_cast<const v8bf*>(stage + (64 * fq + 32 * fb + col) * kRowBytes +
+                                                32 * ks + 16 * g);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        b[tb] = *reinterpret_cast<const v8bf*>(stage + kWRegion +
+                                                (64 * tq + 32 * tb + col) * kRowBytes + 32 * ks +
+                                                16 * g);
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = mfma_bf16(a[fb], b[tb], acc[fb][tb]);
+    }
+    wait_vmcnt(next > c + 2 ? n_mine * (next - c - 2) : 0);
+    block_barrier();
+  }
+
+  // Epilogue. Lane (g, col) of block (fb, tb) holds token 64 tq + 32 tb + col and features
+  // 64 fq + 32 fb + 8 q + 4 g + (0..3), q = 0..3. Their codes go to an LDS tile of 128
+  // token rows (kCodeStride bytes apart: consecutive tokens start 4 banks apart), then
+  // out in 16-byte pieces.
+  const float dk = p.dk[h], dv = p.dv[h];
+  const float d = fq < 2 ? dk : dv;  // features 0..127 are k_nope, 128..255 v
+  const float rr = 1.0f / d;
+  const int64_t kst = static_cast<int64_t>(H) * 192, vst = static_cast<int64_t>(H) * kDv;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int tok = 64 * tq + 32 * tb + col;
+    const int64_t t = t0 + tok;
+    const bool store_bf16 = tok < n_tok && (p.kb != nullptr || p.vb != nullptr);
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb) {
+      uint32_t pr[8];  // the block's 16 values (q, i) as bf16 pairs, element 4 q + i
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // v_cvt_pk_bf16_f32: two fp32 values to bf16, nearest even
+        pr[2 * q] = __builtin_bit_cast(
+            uint32_t, __builtin_convertvector(v2f{acc[fb][tb][4 * q], acc[fb][tb][4 * q + 1]}, v2bf));
+        pr[2 * q + 1] = __builtin_bit_cast(
+            uint32_t,
+            __builtin_convertvector(v2f{acc[fb][tb][4 * q + 2], acc[fb][tb][4 * q + 3]}, v2bf));
+      }
+      const uint4 cd = quant16(pr, d, rr);
+      const uint32_t cw[4] = {cd.x, cd.y, cd.z, cd.w};  // word q: codes of (q, 0..3)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f = 64 * fq + 32 * fb + 8 * q + 4 * g;
+        *reinterpret_cast<uint32_t*>(lds + tok * kCodeStride + f) = cw[q];
+        if (store_bf16) {
+          const uint2 val = make_uint2(pr[2 * q], pr[2 * q + 1]);
+          if (f < kNope) {
+            if (p.kb != nullptr) *reinterpret_cast<uint2*>(p.kb + t * kst + h * 192 + f) = val;
+          } else if (p.vb != nullptr) {
+            *reinterpret_cast<uint2*>(p.vb + t * vst + h * kDv + (f - kNope)) = val;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kTM * 16 / kThreads; ++j) {
+    const int id = tid + kThreads * j;
+    const int tok = id >> 4, pc = id & 15;
+    if (tok < n_tok) {
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + tok * kCodeStride + 16 * pc);
+      const int64_t t = t0 + tok;
+      if (pc < 8)
+        *reinterpret_cast<uint4*>(p.k8 + t * kst + h * 192 + 16 * pc) = v;
+      else
+        *reinterpret_cast<uint4*>(p.v8 + t * vst + h * kDv + 16 * (pc - 8)) = v;
+    }
+  }
+  if (pe_tok < n_tok) {
+    const uint32_t w[8] = {pe_a.x, pe_a.y, pe_a.z, pe_a.w, pe_b.x, pe_b.y, pe_b.z, pe_b.w};
+    const int64_t o = (t0 + pe_tok) * kst + h * 192 + kNope + 16 * pe_pc;
+    *reinterpret_cast<uint4*>(p.k8 + o) = quant16(w, dk, 1.0f / dk);
+    if (p.kb != nullptr) {
+      *reinterpret_cast<uint4*>(p.kb + o) = pe_a;
+      *reinterpret_cast<uint4*>(p.kb + o + 8) = pe_b;
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" int mla_fp8_kv_produce(const void* c_kv, int64_t c_kv_stride, const void* k_pe,
+                                  int64_t k_pe_stride, const void* w_kv_b, int64_t n_tokens,
+                                  int32_t n_heads, int32_t kv_lora_rank, int32_t rope_dim,
+                                  const float* descale_k, const float* descale_v, void* k8,
+                                  void* v8, void* k_bf16, void* v_bf16, void* stream) {
+  if (kv_lora_rank != kLatent || rope_dim != kRope)
+    return mla::fail(MLA_ERR_UNSUPPORTED, "latent rank %d / rope dim %d: only 512 / 64",
+                     kv_lora_rank, rope_dim);
+  if (n_heads < 1) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "n_heads = %d < 1", n_heads);
+  if (n_tokens < 0) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "negative n_tokens");
+  if (n_tokens == 0) return mla::ok();
+  if (c_kv == nullptr || k_pe == nullptr || w_kv_b == nullptr || descale_k == nullptr ||
+      descale_v == nullptr || k8 == nullptr || v8 == nullptr)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (c_kv_stride < kLatent || k_pe_stride < kRope || c_kv_stride % 8 != 0 ||
+      k_pe_stride % 8 != 0 || c_kv_stride >= (1 << 24) || k_pe_stride >= (1 << 24))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT,
+                     "row strides must be multiples of 8 elements, >= the row, < 2^24");
+  if (!mla::aligned16(c_kv) || !mla::aligned16(k_pe) || !mla::aligned16(w_kv_b) ||
+      !mla::aligned16(k8) || !mla::aligned16(v8) || !mla::aligned16(k_bf16) ||
+      !mla::aligned16(v_bf16))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  const int64_t tiles = (n_tokens + kTM - 1) / kTM;
+  if (tiles * n_heads >= (1ll << 31)) return mla::fail(MLA_ERR_UNSUPPORTED, "grid too large");
+  ProducerParams prm{};
+  prm.c_kv = static_cast<const uint16_t*>(c_kv);
+  prm.k_pe = static_cast<const uint16_t*>(k_pe);
+  prm.w = static_cast<const uint16_t*>(w_kv_b);
+  prm.dk = descale_k;
+  prm.dv = descale_v;
+  prm.k8 = static_cast<uint8_t*>(k8);
+  prm.v8 = static_cast<uint8_t*>(v8);
+  prm.kb = static_cast<uint16_t*>(k_bf16);
+  prm.vb = static_cast<uint16_t*>(v_bf16);
+  prm.c_stride = c_kv_stride;
+  prm.pe_stride = k_pe_stride;
+  prm.n_tokens = n_tokens;
+  prm.n_heads = n_heads;
+  prm.xcd_order = (tiles * n_heads) % 8 == 0 ? 1 : 0;
+  hipLaunchKernelGGL(kv_producer_kernel, dim3(static_cast<unsigned>(tiles * n_heads)),
+                     dim3(kThreads), 0, static_cast<hipStream_t>(stream), prm);
+  return mla::check_launch("kv_producer_kernel");
+}

@@ -6,19 +6,18 @@
 // covers up to three tensors (Q, K, V) with their own head dims and descales.
 //
 // Rounding contract: the code is the correctly rounded E4M3 value of the exact
-// quotient x / descale (nearest, ties to even, saturating at +-448, NaN kept).
-// The kernel multiplies by r = 1/descale in fp32, which can be off by up to
-// ~3 ulp, then rounds with integer bit operations. Only when the fp32
-// quotient lies within 16 ulp of an E4M3 rounding boundary M can that differ
-// from the exact result; there the sign of x - M*descale is taken in fp64,
-// where M*descale (5 + 24 significant bits) and the difference are exact.
+// quotient x / descale (nearest, ties to even, saturating at +-448, NaN kept); see
+// quant16 and quant_one for how the device reaches it.
 //
 // HBM-bound: 2 bytes read + 1 byte written per element. Each thread handles
 // 16 consecutive elements of one (token, head) row: two 16-byte loads, one
 // 16-byte store.
 #include "mla_internal.h"
+#include "e4m3_quant.h"
 
 namespace {
+
+using mla::dev::quant_one;
 
 constexpr int kQuantThreads = 256;
 constexpr int kMaxJobs = 3;
@@ -43,55 +42,11 @@ struct QuantParams {
   mla::FastDiv heads;
 };
 
-// One bf16 (bits in the low 16 bits) divided by descale d (r ~ 1/d) to an E4M3 code.
-__device__ __forceinline__ uint32_t quant_one(uint32_t xb, float d, float r) {
-  const uint32_t sign = (xb >> 8) & 0x80u;
-  const uint32_t xa = (xb & 0x7FFFu) << 16;  // |x| as fp32 bits
-  if (xa > 0x7F800000u) return 0x7Fu | sign;  // NaN
-  const float ax = __uint_as_float(xa);
-  const float qf = ax * r;
-  const uint32_t a = __float_as_uint(qf);
-  if (a > 0x43E00000u) return 0x7Eu | sign;  // > 448 (also +Inf): saturate, no boundary nearby
-  uint32_t lower;  // code of the E4M3 value just below (or at) qf
-  bool up, near;
-  float mid;       // the rounding boundary above `lower`
-  if (a >= 0x3C800000u) {  // >= 2^-6: normal E4M3 range
-    lower = (a >> 20) - (120u << 3);
-    const uint32_t low = a & 0xFFFFFu;
-    up = low > 0x80000u;
-    near = (low > 0x80000u ? low - 0x80000u : 0x80000u - low) <= 16u;
-    mid = __uint_as_float((a & ~0xFFFFFu) | 0x80000u);
-  } else {  // subnormal E4M3: multiples of 2^-9
-    const float t = qf * 512.0f;  // exact
-    const float n = floorf(t);
-    const float f = t - n;        // exact
-    lower = static_cast<uint32_t>(n);
-    up = f > 0.5f;
-    near = fabsf(f - 0.5f) <= 0x1p-17f;
-    mid = (n + 0.5f) * 0x1p-9f;  // exact
-  }
-  if (near) {
-    // exact side of the boundary: sign of |x| - mid * d, computed exactly in fp64
-    const double diff = static_cast<double>(ax) - static_cast<double>(mid) * static_cast<double>(d);
-    up = diff > 0.0 || (diff == 0.0 && (lower & 1u));
-  }
-  return (lower + (up ? 1u : 0u)) | sign;
-}
-
 // Dynamic scales: descale = RN_fp32(amax / 448) floored at 2^-126 (1/descale stays
 // finite), or 1 when the head is all zeros (any positive descale gives the same codes).
 __device__ __forceinline__ float descale_of_amax(float amax) {
   if (!(amax > 0.f)) return 1.f;
   return fmaxf(__fdiv_rn(amax, 448.f), 0x1p-126f);
-}
-
-__device__ __forceinline__ uint32_t quant_pack4(uint32_t w0, uint32_t w1, float d, float r) {
-  // w0 holds bf16 elements 0,1 (low, high halves), w1 elements 2,3
-  uint32_t c0 = quant_one(w0 & 0xFFFFu, d, r);
-  uint32_t c1 = quant_one(w0 >> 16, d, r);
-  uint32_t c2 = quant_one(w1 & 0xFFFFu, d, r);
-  uint32_t c3 = quant_one(w1 >> 16, d, r);
-  return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
 }
 
 __global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantParams p) {
@@ -128,11 +83,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantParams
       for (int i = 0; i < 8; ++i)
         w[i] = static_cast<uint32_t>(src[2 * i]) | (static_cast<uint32_t>(src[2 * i + 1]) << 16);
     }
-    uint4 o;
-    o.x = quant_pack4(w[0], w[1], d, r);
-    o.y = quant_pack4(w[2], w[3], d, r);
-    o.z = quant_pack4(w[4], w[5], d, r);
-    o.w = quant_pack4(w[6], w[7], d, r);
+    const uint4 o = mla::dev::quant16(w, d, r);
     *reinterpret_cast<uint4*>(jb.y + static_cast<int64_t>(row) * jb.head_dim + col * 16u) = o;
   }
 }

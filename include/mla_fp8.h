@@ -127,6 +127,40 @@ int mla_fp8_amax_per_head(const void* x, int64_t stride_token, int64_t stride_he
                           int64_t n_tokens, int32_t n_heads, int32_t head_dim,
                           float* amax, void* stream);
 
+/*
+ * Un-absorbed MLA K/V producer fused with the static quantizer. "[ROCm][Kimi-K3]
+ * Fold q_b_proj and W_UK for MLA decode", Purpose: prefill keeps the un-absorbed
+ * form, in which keys and values are expanded from the latent cache per head
+ * (latent rank 512; the 192-wide key head ends in the 64-dim rope part; 12 heads
+ * per rank). The codes follow mla_fp8_quant_static's contract.
+ *
+ *   c_kv          device bf16 latent rows, row t at c_kv + t * c_kv_stride (elements);
+ *                 the first 512 elements of a row are used
+ *   k_pe          device bf16 rope keys (already rotated), row t at k_pe + t * k_pe_stride;
+ *                 the first 64 elements are used, shared by every head
+ *   w_kv_b        device bf16 [n_heads * 256, 512], row-major: rows 256h .. 256h+127 are
+ *                 W_UK[h] (the no-rope key part), rows 256h+128 .. 256h+255 are W_UV[h]
+ *   descale_k/v   device fp32 [n_heads], finite and positive
+ *   k8, v8        device E4M3 codes, contiguous [n_tokens, n_heads, 192] and [.., 128]
+ *   k_bf16/v_bf16 NULL, or device bf16 [n_tokens, n_heads, 192] / [.., 128] that receive
+ *                 the same K and V before quantization (for a BF16 attention path)
+ *
+ *   k_nope[t,h,i] = RN_bf16(sum_j W_UK[h][i][j] * c_kv[t][j]), v[t,h,i] likewise with
+ *   W_UV[h], K[t,h] = [k_nope[t,h] | k_pe[t]], k8 = E4M3(K / descale_k[h]),
+ *   v8 = E4M3(v / descale_v[h]) (exact quotient, nearest even, saturating). The sums
+ *   accumulate in fp32 on the matrix cores, so a bf16 value can differ by one ulp from
+ *   the rounding of the exact sum where that sum lies within the accumulation error of
+ *   a bf16 rounding boundary; the codes are exact for the bf16 values produced.
+ *   kv_lora_rank != 512 or rope_dim != 64 -> MLA_ERR_UNSUPPORTED. NULL pointers,
+ *   pointers not 16-byte aligned, strides below the row length, not multiples of 8 or
+ *   >= 2^24 -> MLA_ERR_INVALID_ARGUMENT. n_tokens == 0 succeeds without a launch.
+ */
+int mla_fp8_kv_produce(const void* c_kv, int64_t c_kv_stride, const void* k_pe,
+                       int64_t k_pe_stride, const void* w_kv_b, int64_t n_tokens,
+                       int32_t n_heads, int32_t kv_lora_rank, int32_t rope_dim,
+                       const float* descale_k, const float* descale_v, void* k8, void* v8,
+                       void* k_bf16, void* v_bf16, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Varlen context-prefill attention                                          */
 /* ------------------------------------------------------------------------ */

@@ -238,3 +238,22 @@ def make_random(seed: int, lens_q, lens_k=None, causal: bool = True, heads: int 
         causal=causal, softmax_scale=1.0 / math.sqrt(D_QK), factors=factors, outlier_mask=masks,
         segment_len=0, description="custom test workload",
     )
+
+
+LATENT = 512
+ROPE = 64
+
+
+def make_latent(seed: int, n_tokens: int, heads: int = N_HEADS):
+    """Latent-cache rows and an expansion weight for the un-absorbed K/V producer.
+
+    Recipe: ``default_rng(seed)``; cache = bf16_RNE(standard normal [n_tokens, 576]) (the
+    512 latent values of a token followed by its 64 rope-key values, one row per token,
+    as a normalised latent and a rotated rope key would be); then
+    w = bf16_RNE(standard normal [heads * 256, 512] / sqrt(512)), so that every expanded
+    value is about unit-variance. Returns (cache bits [T, 576], w bits [heads * 256, 512]).
+    """
+    rng = np.random.default_rng(seed)
+    cache = f32_to_bf16_bits(rng.standard_normal((n_tokens, LATENT + ROPE), dtype=np.float32))
+    w = rng.standard_normal((heads * 256, LATENT), dtype=np.float32) * np.float32(1 / math.sqrt(LATENT))
+    return cache, f32_to_bf16_bits(w)

@@ -120,6 +120,31 @@ def test_prefill_bf16_validation_before_launch(lib):
     assert _prefill_bf16(lib, batch=0) == binding.MLA_OK
 
 
+def test_kv_produce_validation_before_launch(lib):
+    f = lib.mla_fp8_kv_produce
+    A = 1 << 12
+    ok = dict(c=A, cs=512, pe=A, ps=64, w=A, n=16, h=12, r=512, rope=64, dk=A, dv=A, k8=A, v8=A,
+              kb=None, vb=None, st=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(r=256) == binding.MLA_ERR_UNSUPPORTED
+    assert call(rope=32) == binding.MLA_ERR_UNSUPPORTED
+    assert call(h=0) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert call(n=-1) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert call(c=None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert call(dv=None) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert call(cs=500) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert call(ps=60) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert call(cs=1 << 24) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert call(k8=A + 8) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert call(kb=A + 2) == binding.MLA_ERR_INVALID_ARGUMENT
+    assert call(n=0, c=None, k8=None) == binding.MLA_OK
+
+
 def test_quant_validation_before_launch(lib):
     job = binding.QuantJob(1 << 12, 192 * 12, 192, 10, 192, 1 << 12, 1 << 12)
     jobs = (binding.QuantJob * 3)(job, job, job)
