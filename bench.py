@@ -39,12 +39,13 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources with // comments and blank lines removed, so that the
-    counter record stays valid across comment-only edits."""
+    """Hash of the FP8 prefill kernel's sources (the kernel file and the headers it
+    includes), with // comments and blank lines removed, so that the counter record
+    stays valid across comment-only edits and changes to other kernels."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_mla_context_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    for fn in ("device_common.h", "mla_internal.h", "prefill_fp8.hip"):
         with open(os.path.join(csrc, fn)) as f:
             text = f.read()
         code = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
