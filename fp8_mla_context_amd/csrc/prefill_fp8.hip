@@ -11,11 +11,12 @@
 //    workgroups and one's VALU work fills the other's MFMA time. Workgroups are ordered
 //    heaviest first: the flattened block index walks query tiles from the last (most
 //    keys under a causal mask) to the first, with heads and sequences fastest.
-//  * 64-key K/V tiles live in three rotating LDS buffers, filled by global->LDS DMA
-//    (global_load_lds_dwordx4, no register staging). K rows are padded to 208 bytes; V
-//    rows are 128 bytes with XOR-swizzled 16-byte chunks (see v_swizzle). Iteration t
-//    issues the loads of K(t+3) and V(t+1) and computes, interleaved, the PV MFMAs of
-//    tile t-1, the S MFMAs of tile t+1 and the softmax of tile t. One barrier per tile.
+//  * 64-key K tiles live in three rotating LDS buffers and FP8 V tiles in two, filled by
+//    global->LDS DMA (global_load_lds_dwordx4, no register staging). K rows are padded to
+//    208 bytes; V rows are 128 bytes with XOR-swizzled 16-byte chunks (see v_swizzle).
+//    Iteration t issues the loads of K(t+3) and V(t+1) and computes, interleaved, the PV
+//    MFMAs of tile t-1, the S MFMAs of tile t+1 and the softmax of tile t; after a
+//    barrier the waves convert V tile t to bf16 V^T for the next iteration's PV.
 //  * S^T = K * Q^T on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32): the Q fragment
 //    (32 rows x 192) stays in registers as the B operand, K rows are read from LDS as
 //    the A operand. In the 32x32 accumulator layout every lane holds one query row
@@ -26,19 +27,21 @@
 //    per element. The reference max m moves only when a row's max exceeds it by more
 //    than kRescaleSlack (a rare wave-uniform branch rescales l, and O once the previous
 //    tile's PV has been added).
-//  * O^T = V^T * P^T on the same MFMA with P in two E4M3 terms (hi + lo, both summed
-//    into the same fp32 O): one E4M3 term carries up to 2^-4 relative error per weight,
-//    which the output tolerance does not allow on diffuse heads. The split uses f16 bit
-//    arithmetic (see softmax_group). The accumulator layout of S^T already is the B
-//    operand (lane = query row, bytes = 32 keys). The V^T A operand comes from
-//    ds_read_b64_tr_b8: within each 16-lane group, output lane i receives byte i % 8 of
-//    the 8-byte windows addressed by lanes 2b + i/8 (b = 0..7); with lanes 2b and 2b+1
-//    pointing at the same key row and at dims d0 and d0 + 8, lane i gets dim d0 + i of
-//    8 keys, in the key order of the P operand.
+//  * O^T = V^T * P^T on v_mfma_f32_32x32x16_bf16 with P rounded to bf16 (one term: an
+//    E4M3 P carries up to 2^-4 relative error per weight, more than the output tolerance
+//    allows on diffuse heads, and two E4M3 terms cost more VALU work than this path).
+//    Registers 8 ck .. 8 ck + 7 of an S accumulator are one P^T B operand (16 keys). V
+//    stays FP8 in HBM and LDS: each wave reads its 32-dim block of the tile with
+//    ds_read_b64_tr_b8 (within each 16-lane group, output lane i receives byte i % 8 of
+//    the 8-byte windows addressed by lanes 2b + i/8, so lane i gets dim d0 + i of 8 keys
+//    in the key order of the P operand), converts it exactly to bf16
+//    (v_cvt_scalef32_pk_bf16_fp8) and stores it as V^T rows; the keys a lane converts
+//    are exactly those its own PV A operands need, so every A operand is one 16-byte
+//    read. The conversion is shared by the workgroup: 16 conversions per lane per tile.
 //  * Causal (bottom-right aligned: key j visible to row i iff j <= i + Lk - Lq):
 //    a wave skips tiles past its last visible key; only tiles that cross the
 //    diagonal or the ragged end are masked element-wise.
-//  * Epilogue: out = O * dv / (256 l) in bf16 (fp32 for the partials of a chunked pass),
+//  * Epilogue: out = O * dv / l in bf16 (fp32 for the partials of a chunked pass),
 //    lse = ln2 * (m + log2 l).
 #include "mla_internal.h"
 #include "device_common.h"
@@ -52,7 +55,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kDqk = 192;
 constexpr int kDv = 128;
@@ -68,13 +72,15 @@ constexpr int kKStride = 208;     // LDS bytes per K row: 192 + 16 (8 consecutiv
 constexpr int kVStride = 128;     // LDS bytes per V row, 16-byte chunks XOR-swizzled by key
 constexpr int kKTile = kBN * kKStride;
 constexpr int kVTile = kBN * kVStride;
+// bf16 V^T of one tile: one row per dim, 64 keys (two halves of 32, see the header) + pad;
+// rows 144 bytes apart, so the 16-byte reads of 16 consecutive dims hit distinct banks
+constexpr int kVtStride = 144;
+constexpr int kVtBytes = kDv * kVtStride;
+constexpr int kLdsBytes = 2 * (kKTile + kVTile + kVtBytes);  // 79872: two workgroups per CU
 constexpr int kKChunks = kBN * kDqk / 16;  // 768 16-byte chunks per K tile
 constexpr float kLn2 = 0.69314718055994530942f;
-// P = 2^(logit*log2e - m) <= 2^kRescaleSlack; its E4M3 codes stand for 256 * P, so the
-// largest weight maps near 2^8, small weights stay clear of E4M3 subnormals, and
-// 256 * P <= 2^8.75 < 448.
-constexpr float kRescaleSlack = 0.75f;
-constexpr half2_t kOnes2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+// P = 2^(logit*log2e - m) <= 2^kRescaleSlack is a bf16 operand; the slack only bounds O.
+constexpr float kRescaleSlack = 8.0f;
 
 struct PrefillParams {
   const uint8_t* q;
@@ -119,6 +125,10 @@ __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+__device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   const v4i a = *reinterpret_cast<const v4i*>(p);
   const v4i b = *reinterpret_cast<const v4i*>(p + 16);
@@ -154,8 +164,8 @@ __device__ __forceinline__ int v_swizzle(int key) { return (key & 3) | (((key >>
 template <int kNSeg>
 __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(PrefillParams p,
                                                                         SegTable<kNSeg> st) {
-  // three K/V tile buffers: tile t is in buffer t % 3
-  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * (kKTile + kVTile)];
+  // K tile t, FP8 V tile t and bf16 V^T of tile t each in buffer t % 2 of their kind
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -265,23 +275,20 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   // Tile fill by direct global->LDS loads (global_load_lds_dwordx4): one wave
   // instruction writes 64 consecutive 16-byte LDS slots, lane l to slot l, from any
   // per-lane global address. A K tile is 64 rows x 13 slots (12 data + 1 pad), a V tile
-  // 64 rows x 9 slots (8 data + 1 pad); the 13 K and the 9 V instructions of a tile are
+  // 64 rows x 8 slots (chunks swizzled); the 13 K and the 8 V instructions of a tile are
   // dealt round-robin to the waves. Pad slots load a duplicate chunk; rows past the
   // sequence load its last row (K logits there are masked to -inf and their P is 0, so
   // the duplicate never contributes, and no uninitialised bytes are ever read).
   //
-  // Schedule: tile t lives in buffer t % 3. Iteration t reads K(t+1) (S of the next
-  // tile) and V(t-1) (PV of the previous tile) and issues K(t+3) and V(t+1), into the
-  // buffers that K(t) and V(t-2) left at the previous barrier. Everything iteration t+1
-  // reads (K(t+2), V(t)) was issued one iteration earlier, so the wait before the
-  // barrier lets this iteration's loads stay in flight: each wave waits until at most
-  // the number of loads it issued this iteration is outstanding (loads complete in order).
+  // Schedule: K, V and V^T of tile t live in buffer t % 2 of their kind. Iteration t
+  // reads K(t+1) (S of the next tile), V(t) (converted to V^T) and the V^T of tile t-1
+  // (PV of the previous tile), and issues K(t+2) and V(t+1) at its start, into the
+  // buffers that K(t) and V(t-1) left at the previous barrier; they land before the
+  // iteration's closing barrier.
   constexpr int kKInstr = kBN * (kKStride / 16) / 64;  // 13
   constexpr int kVInstr = kBN * (kVStride / 16) / 64;  // 8
   constexpr int kPerK = (kKInstr + kWaves - 1) / kWaves;
   constexpr int kPerV = (kVInstr + kWaves - 1) / kWaves;
-  const int n_k_instr = (kKInstr - wave + kWaves - 1) / kWaves;  // K loads of this wave per tile
-  const int n_v_instr = (kVInstr - wave + kWaves - 1) / kWaves;  // V loads
   // Slot j of a K (V) tile (instruction i = wave + j * kWaves): this lane's tile row and
   // the byte offset of its chunk within the row. Full tiles use a wave-uniform base plus
   // row * row_stride + chunk (< 2^31, checked on the host); the ragged last tile clamps rows.
@@ -307,14 +314,16 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     const int2 rc = dma_row(j, false);
     dma_off_v[j] = static_cast<uint32_t>(rc.x) * v_rs32 + static_cast<uint32_t>(rc.y);
   }
-  auto kbuf = [&](int t) { return lds + (t % 3) * (kKTile + kVTile); };
+  auto kbuf = [&](int t) { return lds + (t & 1) * kKTile; };
+  auto vbuf = [&](int t) { return lds + 2 * kKTile + (t & 1) * kVTile; };
+  auto vtbuf = [&](int t) { return lds + 2 * (kKTile + kVTile) + (t & 1) * kVtBytes; };
   // issue this wave's loads of the K (is_k) or V part of tile t
   auto issue = [&](int t, bool is_k) {
     const int kt = t * kBN;
     const int64_t rs = is_k ? k_rs : v_rs;
     const uint32_t rs32 = is_k ? k_rs32 : v_rs32;
     const uint8_t* base = uniform_ptr((is_k ? kbase : vbase) + static_cast<int64_t>(kt) * rs);
-    const uint32_t dst0 = lds_address(kbuf(t) + (is_k ? 0 : kKTile));
+    const uint32_t dst0 = lds_address(is_k ? kbuf(t) : vbuf(t));
     const int n_instr = is_k ? kKInstr : kVInstr;
     const bool full = kt + kBN <= Lk;
 #pragma unroll
@@ -339,12 +348,14 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   const int vt_key0 = 8 * (tb >> 2) + 4 * (grp >> 1) + (tb & 3);
   const int vt_off = vt_key0 * kVStride + 16 * ((grp & 1) ^ v_swizzle(vt_key0)) + 8 * tp;
 
-  // prologue: K(0), V(0), K(1) in LDS, K(2) in flight, S of tile 0 computed
-  int in_flight = 0;
+  // prologue: K(0), V(0), K(1) in LDS, S of tile 0 computed, the V^T buffer that
+  // iteration 0 reads zeroed (it multiplies a zero P: no uninitialised LDS reaches an MFMA)
+  for (int i = tid; i < kVtBytes / 16; i += kThreads)
+    reinterpret_cast<uint4*>(vtbuf(1))[i] = make_uint4(0, 0, 0, 0);
   if (n_tiles > 0) { issue(0, true); issue(0, false); }
   if (n_tiles > 1) issue(1, true);
-  if (n_tiles > 2) { issue(2, true); in_flight += n_k_instr; }
-  wait_vmcnt(in_flight);
+  wait_vmcnt(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the zero stores have landed
   // retire the Q-fragment loads here on every path (an empty asm that reads the
   // registers), so that no compiler-inserted memory wait is left inside the loop
 #pragma unroll
@@ -352,47 +363,56 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   block_barrier();
   v16f s_cur[2];
   if (wave_tiles > 0) qk_tile(kbuf(0), col, g, qf, s_cur);
+  block_barrier();  // K(0) is read: iteration 0 may load K(2) into its buffer
 
-  // Softmax of one group of 4 keys (w = 0..7) of this lane's 32: P = 2^(c*s + nbias) <= 2^slack,
-  // rounded toward zero to f16 pairs. The f16 bit pattern of P read at bits 7..14 is the
-  // E4M3 code of 256 * P with its mantissa truncated to 3 bits (f16 and E4M3 exponent
-  // biases differ by 8, and f16 subnormals map onto E4M3 subnormals), so the hi term is
-  // a shift and a byte permute. lo = P - hi is exact in f16; its code is rounded to
-  // 3 mantissa bits (half away from zero) by adding 2^6 at bit 0 before the same
-  // extraction. hi + lo is 256 * P within 2^-7 relative; the row sum adds the f16 P.
-  auto softmax_exp = [&](const v16f(&sc)[2], float nbias, int w) {
-    float4 pw;
-    pw.x = __builtin_amdgcn_exp2f(fmaf(sc[(4 * w) >> 4][(4 * w) & 15], c, nbias));
-    pw.y = __builtin_amdgcn_exp2f(fmaf(sc[(4 * w + 1) >> 4][(4 * w + 1) & 15], c, nbias));
-    pw.z = __builtin_amdgcn_exp2f(fmaf(sc[(4 * w + 2) >> 4][(4 * w + 2) & 15], c, nbias));
-    pw.w = __builtin_amdgcn_exp2f(fmaf(sc[(4 * w + 3) >> 4][(4 * w + 3) & 15], c, nbias));
-    return pw;
+  static_assert(kWaves == 4, "each wave converts one 32-dim block of V");
+  const v2bf ones2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  // Softmax of 16 keys: S block b2, accumulator registers 8 ck .. 8 ck + 7. P = 2^(c*s +
+  // nbias) rounded to bf16 (nearest even) is the B operand of one bf16 PV MFMA (MFMA
+  // k-index 8 g + i stands for key 32 b2 + 16 ck + 8 (i / 4) + 4 g + i % 4); the row sum
+  // adds the rounded weights.
+  auto softmax_chunk = [&](const v16f(&sc)[2], float nbias, int b2, int ck) {
+    v8bf pb;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[b2][8 * ck + i], c, nbias));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[b2][8 * ck + i + 1], c, nbias));
+      const v2bf pr = __builtin_convertvector(v2f{e0, e1}, v2bf);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l_run, false);
+      pb[i] = pr[0];
+      pb[i + 1] = pr[1];
+    }
+    // pin the chunk here: its result is only read in the next iteration, and the compiler
+    // would otherwise sink it below the MFMAs it is meant to overlap
+    asm volatile("" ::"v"(pb), "v"(l_run));
+    return pb;
   };
-  auto softmax_pack = [&](const float4& pw, int w, v8i& phi, v8i& plo) {
-    const half2_t p01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pw.x, pw.y));
-    const half2_t p23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pw.z, pw.w));
-    l_run = __builtin_amdgcn_fdot2(p01, kOnes2, l_run, false);
-    l_run = __builtin_amdgcn_fdot2(p23, kOnes2, l_run, false);
-    const uint32_t u01 = __builtin_bit_cast(uint32_t, p01);
-    const uint32_t u23 = __builtin_bit_cast(uint32_t, p23);
-    // (u << 1) moves bits 7..14 of each half to bytes 1 and 3
-    phi[w] = static_cast<int>(__builtin_amdgcn_perm(u23 << 1, u01 << 1, 0x07050301u));
-    const half2_t lo01 = p01 - __builtin_bit_cast(half2_t, u01 & 0xFF80FF80u);
-    const half2_t lo23 = p23 - __builtin_bit_cast(half2_t, u23 & 0xFF80FF80u);
-    const uint32_t r01 = (__builtin_bit_cast(uint32_t, lo01) << 1) + 0x00800080u;
-    const uint32_t r23 = (__builtin_bit_cast(uint32_t, lo23) << 1) + 0x00800080u;
-    plo[w] = static_cast<int>(__builtin_amdgcn_perm(r23, r01, 0x07050301u));
-    // pin the group here: its results are only read in the next iteration, and the
-    // compiler would otherwise sink it below the MFMAs it is meant to overlap
-    asm volatile("" ::"v"(phi[w]), "v"(plo[w]), "v"(l_run));
-  };
-  auto vt_operand = [&](const uint8_t* vl, int db) {
-    const uint8_t* vp = vl + (vt_off ^ (db << 5));
+  // The transposed reads give lane (g, col) dim 32 db + col of the 32 keys
+  // 32 b2 + 8 q + 4 g + i at byte 16 b2 + 4 q + i (b2, q, i = 0..1, 0..3, 0..3).
+  // Wave w converts dims 32 w .. 32 w + 31 of FP8 V tile t to the bf16 V^T buffer: row
+  // 32 w + col, bytes 64 g .. 64 g + 63 hold the lane's 32 keys in the order above. The
+  // keys that lane (g, col) converts are exactly those its PV A operands need, so PV
+  // operand (db, b2, ck) is the 16 bytes at 64 g + 32 b2 + 16 ck of row 32 db + col.
+  auto convert_half = [&](int t, int half) {  // the keys of S block b2 = half
+    const uint8_t* vp = vbuf(t) + (vt_off ^ (wave << 5)) + 32 * half * kVStride;
+    uint8_t* dst = vtbuf(t) + (32 * wave + col) * kVtStride + 64 * g + 32 * half;
     const v2i r0 = read_tr8(vp);
     const v2i r1 = read_tr8(vp + 16 * kVStride);
-    const v2i r2 = read_tr8(vp + 32 * kVStride);
-    const v2i r3 = read_tr8(vp + 48 * kVStride);
-    return v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+    const int raw[4] = {r0.x, r0.y, r1.x, r1.y};
+    uint32_t cv[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      cv[2 * w] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[w], 1.0f, false));
+      cv[2 * w + 1] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[w], 1.0f, true));
+    }
+    *reinterpret_cast<uint4*>(dst) = make_uint4(cv[0], cv[1], cv[2], cv[3]);
+    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(cv[4], cv[5], cv[6], cv[7]);
+  };
+  auto vt_read = [&](const uint8_t* vt, int db, int b2, int ck) {
+    return *reinterpret_cast<const v8bf*>(vt + (32 * db + col) * kVtStride + 64 * g + 32 * b2 +
+                                          16 * ck);
   };
   // K operand of S MFMA k (k = 0..5 alternates the two 32-key blocks: consecutive MFMAs
   // write different accumulators)
@@ -400,31 +420,30 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     const int b2 = k & 1, kb = k >> 1;
     return load32(kl + (32 * b2 + col) * kKStride + 64 * kb + 32 * g);
   };
-  // One software-pipelined iteration. S of tile it is in s_cur, the E4M3 P of tile it-1
-  // in (phi_p, plo_p). The iteration interleaves three independent streams: the 8 PV
-  // MFMAs of tile it-1 (hi and lo term of each 32-dim block), the 6 S MFMAs of tile it+1
-  // and the softmax of tile it, whose P goes to (phi_c, plo_c). A wave runs
-  // wave_tiles + 1 iterations: the last one is a fully masked tile that only completes
-  // the PV of the wave's last tile; on iteration 0 the previous P is zero (the PV adds
-  // nothing). S computed from a buffer past the wave's range is never used.
-  auto step = [&](int it, v16f(&s_cur)[2], v16f(&s_next)[2], const v8i& phi_p, const v8i& plo_p,
-                  v8i& phi_c, v8i& plo_c) {
+  // One software-pipelined iteration. S of tile it is in s_c, the bf16 P of tile it-1 in
+  // pb_p and its V^T in V^T buffer (it-1) % 2 (on iteration 0: zero P and a zeroed
+  // buffer). The iteration loads K(it+2) and V(it+1) into the buffers that K(it) and
+  // V(it-1) left at the previous barrier, and interleaves the 16 PV MFMAs of tile it-1,
+  // the 6 S MFMAs of tile it+1, the softmax of tile it (P to pb_c) and the conversion of
+  // V tile it to V^T buffer it % 2. A wave runs wave_tiles + 1 active iterations: the last
+  // one is a fully masked tile that only completes the PV of its last tile. Every wave
+  // takes part in every conversion. One barrier per iteration; all loads land before it.
+  auto step = [&](int it, v16f(&s_c)[2], v16f(&s_n)[2], const v8bf(&pb_p)[4], v8bf(&pb_c)[4]) {
     const bool active = it < wave_iters;
+    const bool convert = it < n_tiles;
     const uint8_t* kl = kbuf(it + 1);
-    const uint8_t* vl = kbuf(it > 0 ? it - 1 : 0) + kKTile;
-    // operands of the first MFMAs, read before anything else so that the loads below
-    // and the max reduction cover their latency
-    v8i va0, va1, va2, va3, ka, kb;
+    const uint8_t* vt = vtbuf(it - 1);
+    v8bf va[2];
+    v8i ka, kb;
     if (active) {
-      va0 = vt_operand(vl, 0);
-      va1 = vt_operand(vl, 1);
+      va[0] = vt_read(vt, 0, 0, 0);
+      va[1] = vt_read(vt, 1, 0, 0);
       ka = k_operand(kl, 0);
       kb = k_operand(kl, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    int issued = 0;
-    if (it + 3 < n_tiles) { issue(it + 3, true); issued += n_k_instr; }
-    if (it + 1 < n_tiles) { issue(it + 1, false); issued += n_v_instr; }
+    if (it + 2 < n_tiles) issue(it + 2, true);
+    if (it + 1 < n_tiles) issue(it + 1, false);
 
     if (active) {
       const int kt = it * kBN;
@@ -440,13 +459,13 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kt + 32 * b2 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (all || key >= Lk || (causal && key > my_row + off)) s_cur[b2][r] = -INFINITY;
+            if (all || key >= Lk || (causal && key > my_row + off)) s_c[b2][r] = -INFINITY;
           }
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
-        mx = vmax3(mx, vmax3(s_cur[0][r], s_cur[0][r + 1], s_cur[1][r]), s_cur[1][r + 1]);
+        mx = vmax3(mx, vmax3(s_c[0][r], s_c[0][r + 1], s_c[1][r]), s_c[1][r + 1]);
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                          false, false);
@@ -468,62 +487,36 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
       }
       const float nbias = (m_run == -INFINITY) ? 0.f : -m_run;
 
-      // 14 MFMA slots; each is followed by the exponentials of one softmax group (E) or
-      // the split and pack of the group whose exponentials were taken two slots earlier (P)
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s_next[b2][r] = 0.f;
-      float4 e_a = softmax_exp(s_cur, nbias, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      o[0] = mfma_f8(va0, phi_p, o[0]);                      // PV hi, dims 0-31
-      float4 e_b = softmax_exp(s_cur, nbias, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      s_next[0] = mfma_f8(ka, qf[0], s_next[0]);             // S, keys 0-31, dims 0-63
-      ka = k_operand(kl, 2);
-      softmax_pack(e_a, 0, phi_c, plo_c);
-      __builtin_amdgcn_sched_barrier(0);
-      o[1] = mfma_f8(va1, phi_p, o[1]);                      // PV hi, dims 32-63
-      e_a = softmax_exp(s_cur, nbias, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      s_next[1] = mfma_f8(kb, qf[0], s_next[1]);             // S, keys 32-63, dims 0-63
-      kb = k_operand(kl, 3);
-      softmax_pack(e_b, 1, phi_c, plo_c);
-      __builtin_amdgcn_sched_barrier(0);
-      o[0] = mfma_f8(va0, plo_p, o[0]);                      // PV lo, dims 0-31
-      va2 = vt_operand(vl, 2);
-      e_b = softmax_exp(s_cur, nbias, 3);
-      __builtin_amdgcn_sched_barrier(0);
-      s_next[0] = mfma_f8(ka, qf[1], s_next[0]);             // dims 64-127
-      ka = k_operand(kl, 4);
-      softmax_pack(e_a, 2, phi_c, plo_c);
-      __builtin_amdgcn_sched_barrier(0);
-      o[1] = mfma_f8(va1, plo_p, o[1]);                      // PV lo, dims 32-63
-      va3 = vt_operand(vl, 3);
-      e_a = softmax_exp(s_cur, nbias, 4);
-      __builtin_amdgcn_sched_barrier(0);
-      o[2] = mfma_f8(va2, phi_p, o[2]);                      // PV hi, dims 64-95
-      softmax_pack(e_b, 3, phi_c, plo_c);
-      __builtin_amdgcn_sched_barrier(0);
-      s_next[1] = mfma_f8(kb, qf[1], s_next[1]);
-      kb = k_operand(kl, 5);
-      e_b = softmax_exp(s_cur, nbias, 5);
-      __builtin_amdgcn_sched_barrier(0);
-      o[3] = mfma_f8(va3, phi_p, o[3]);                      // PV hi, dims 96-127
-      softmax_pack(e_a, 4, phi_c, plo_c);
-      __builtin_amdgcn_sched_barrier(0);
-      s_next[0] = mfma_f8(ka, qf[2], s_next[0]);             // dims 128-191
-      e_a = softmax_exp(s_cur, nbias, 6);
-      __builtin_amdgcn_sched_barrier(0);
-      o[2] = mfma_f8(va2, plo_p, o[2]);                      // PV lo, dims 64-95
-      softmax_pack(e_b, 5, phi_c, plo_c);
-      __builtin_amdgcn_sched_barrier(0);
-      s_next[1] = mfma_f8(kb, qf[2], s_next[1]);
-      e_b = softmax_exp(s_cur, nbias, 7);
-      __builtin_amdgcn_sched_barrier(0);
-      o[3] = mfma_f8(va3, plo_p, o[3]);                      // PV lo, dims 96-127
-      softmax_pack(e_a, 6, phi_c, plo_c);
-      softmax_pack(e_b, 7, phi_c, plo_c);
+        for (int r = 0; r < 16; ++r) s_n[b2][r] = 0.f;
+      // PV MFMA j covers dims 32 (j & 3) .. + 31 and key chunk q = j >> 2 (b2 = q >> 1,
+      // ck = q & 1); softmax chunk q follows PV MFMA 4 q + 1, S MFMA q follows PV MFMA
+      // 4 q + 3, the two conversion halves follow PV MFMAs 6 and 10
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        o[j & 3] = mfma_bf16(va[j & 1], pb_p[j >> 2], o[j & 3]);
+        if (j + 2 < 16) va[j & 1] = vt_read(vt, (j + 2) & 3, (j + 2) >> 3, ((j + 2) >> 2) & 1);
+        if ((j & 3) == 1) {
+          const int q = j >> 2;
+          pb_c[q] = softmax_chunk(s_c, nbias, q >> 1, q & 1);
+        }
+        if ((j & 3) == 3) {
+          const int k = j >> 2;  // S MFMA k: block k & 1, dims 64 (k >> 1) ..
+          if (k & 1) {
+            s_n[1] = mfma_f8(kb, qf[k >> 1], s_n[1]);
+            kb = k_operand(kl, k + 2);
+          } else {
+            s_n[0] = mfma_f8(ka, qf[k >> 1], s_n[0]);
+            ka = k_operand(kl, k + 2);
+          }
+        }
+        if (convert && (j == 6 || j == 10)) convert_half(it, j == 10);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s_n[0] = mfma_f8(ka, qf[2], s_n[0]);
+      s_n[1] = mfma_f8(kb, qf[2], s_n[1]);
 
       if (rescale) {
         // alpha passes through an opaque asm so that the multiplies stay in this rare
@@ -534,16 +527,21 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
+    } else if (convert) {
+      convert_half(it, 0);
+      convert_half(it, 1);
     }
-    wait_vmcnt(issued);  // K(it+2) and V(it) have landed; this iteration's loads may fly
+    wait_vmcnt(0);  // K(it+2) and V(it+1) have landed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // so have the V^T stores
     block_barrier();
   };
 
   v16f s_alt[2];
-  v8i phi_a = {0, 0, 0, 0, 0, 0, 0, 0}, plo_a = phi_a, phi_b = phi_a, plo_b = phi_a;
+  v8bf pb_a[4] = {v8bf{}, v8bf{}, v8bf{}, v8bf{}};
+  v8bf pb_b[4] = {v8bf{}, v8bf{}, v8bf{}, v8bf{}};
   for (int it = 0; it <= n_tiles; it += 2) {
-    step(it, s_cur, s_alt, phi_a, plo_a, phi_b, plo_b);
-    if (it + 1 <= n_tiles) step(it + 1, s_alt, s_cur, phi_b, plo_b, phi_a, plo_a);
+    step(it, s_cur, s_alt, pb_a, pb_b);
+    if (it + 1 <= n_tiles) step(it + 1, s_alt, s_cur, pb_b, pb_a);
   }
 
   // epilogue: this lane holds row my_row, dims 32*db + 8*(r/4) + 4*g + r%4
@@ -554,8 +552,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
   if (row_ok) {
-    // O holds 256 * sum P v (the E4M3 codes of P are 256 * P)
-    const float inv = (l_tot > 0.f) ? p.dv[h] / (256.f * l_tot) : 0.f;
+    // O holds sum P v with v the decoded V codes (their descale is applied here)
+    const float inv = (l_tot > 0.f) ? p.dv[h] / l_tot : 0.f;
     const int64_t obase = (q0 + my_row) * (static_cast<int64_t>(H) * kDv) + h * kDv;
     if (p.out_f32) {
       float* op = static_cast<float*>(out_ptr) + obase;
