@@ -425,21 +425,23 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   // buffer). The iteration loads K(it+2) and V(it+1) into the buffers that K(it) and
   // V(it-1) left at the previous barrier, and interleaves the 16 PV MFMAs of tile it-1,
   // the 6 S MFMAs of tile it+1, the softmax of tile it (P to pb_c) and the conversion of
-  // V tile it to V^T buffer it % 2. A wave runs wave_tiles + 1 active iterations: the last
-  // one is a fully masked tile that only completes the PV of its last tile. Every wave
-  // takes part in every conversion. One barrier per iteration; all loads land before it.
+  // V tile it to V^T buffer it % 2. LDS operands are read three PV MFMAs (V^T) or one S
+  // MFMA (K, three PV MFMAs earlier) ahead of use. A wave runs wave_tiles + 1 active
+  // iterations: the last one is a fully masked tile that only completes the PV of its
+  // last tile. Every wave takes part in every conversion. One barrier per iteration; all
+  // loads land before it.
   auto step = [&](int it, v16f(&s_c)[2], v16f(&s_n)[2], const v8bf(&pb_p)[4], v8bf(&pb_c)[4]) {
     const bool active = it < wave_iters;
     const bool convert = it < n_tiles;
     const uint8_t* kl = kbuf(it + 1);
     const uint8_t* vt = vtbuf(it - 1);
-    v8bf va[2];
-    v8i ka, kb;
+    v8bf va[3];
+    v8i ka;
     if (active) {
       va[0] = vt_read(vt, 0, 0, 0);
       va[1] = vt_read(vt, 1, 0, 0);
+      va[2] = vt_read(vt, 2, 0, 0);
       ka = k_operand(kl, 0);
-      kb = k_operand(kl, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (it + 2 < n_tiles) issue(it + 2, true);
@@ -492,31 +494,25 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
 #pragma unroll
         for (int r = 0; r < 16; ++r) s_n[b2][r] = 0.f;
       // PV MFMA j covers dims 32 (j & 3) .. + 31 and key chunk q = j >> 2 (b2 = q >> 1,
-      // ck = q & 1); softmax chunk q follows PV MFMA 4 q + 1, S MFMA q follows PV MFMA
-      // 4 q + 3, the two conversion halves follow PV MFMAs 6 and 10
+      // ck = q & 1); S MFMAs 0..4 follow PV MFMAs 1, 4, 7, 10, 13 and S MFMA 5 the last;
+      // softmax chunk q follows PV MFMA 4 q + 3, the conversion halves PV MFMAs 5 and 9
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        o[j & 3] = mfma_bf16(va[j & 1], pb_p[j >> 2], o[j & 3]);
-        if (j + 2 < 16) va[j & 1] = vt_read(vt, (j + 2) & 3, (j + 2) >> 3, ((j + 2) >> 2) & 1);
-        if ((j & 3) == 1) {
+        o[j & 3] = mfma_bf16(va[j % 3], pb_p[j >> 2], o[j & 3]);
+        if (j + 3 < 16) va[j % 3] = vt_read(vt, (j + 3) & 3, (j + 3) >> 3, ((j + 3) >> 2) & 1);
+        if (j % 3 == 1) {  // S MFMA k = j / 3 (k = 0..4), then the operand of k + 1
+          const int k = j / 3;
+          s_n[k & 1] = mfma_f8(ka, qf[k >> 1], s_n[k & 1]);
+          ka = k_operand(kl, k + 1);
+        }
+        if ((j & 3) == 3) {
           const int q = j >> 2;
           pb_c[q] = softmax_chunk(s_c, nbias, q >> 1, q & 1);
         }
-        if ((j & 3) == 3) {
-          const int k = j >> 2;  // S MFMA k: block k & 1, dims 64 (k >> 1) ..
-          if (k & 1) {
-            s_n[1] = mfma_f8(kb, qf[k >> 1], s_n[1]);
-            kb = k_operand(kl, k + 2);
-          } else {
-            s_n[0] = mfma_f8(ka, qf[k >> 1], s_n[0]);
-            ka = k_operand(kl, k + 2);
-          }
-        }
-        if (convert && (j == 6 || j == 10)) convert_half(it, j == 10);
+        if (convert && (j == 5 || j == 9)) convert_half(it, j == 9);
         __builtin_amdgcn_sched_barrier(0);
       }
-      s_n[0] = mfma_f8(ka, qf[2], s_n[0]);
-      s_n[1] = mfma_f8(kb, qf[2], s_n[1]);
+      s_n[1] = mfma_f8(ka, qf[2], s_n[1]);  // S MFMA 5
 
       if (rescale) {
         // alpha passes through an opaque asm so that the multiplies stay in this rare
