@@ -46,8 +46,11 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kDqk = 192;
 constexpr int kDv = 128;
-constexpr int kWaves = 4;
-constexpr int kWgPerCu = 2;
+#ifndef MLA_BF16_WAVES
+#define MLA_BF16_WAVES 4
+#endif
+constexpr int kWaves = MLA_BF16_WAVES;  // waves per workgroup (4 or 8)
+constexpr int kWgPerCu = 8 / kWaves;    // resident workgroups per CU (2 waves per SIMD)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 32;           // keys per tile
@@ -67,7 +70,7 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr int kAhead = MLA_BF16_AHEAD;  // LDS operand prefetch distance, in MFMAs
 static_assert(kAhead >= 1 && kAhead <= 4, "prefetch distance");
 static_assert(kBN * kKSlots <= kKInstr * 64, "K tile slots");
-static_assert(2 * 3 * kStage <= 160 * 1024, "two workgroups per CU");
+static_assert(kWgPerCu * 3 * kStage <= 160 * 1024, "resident workgroups fit the LDS");
 
 struct Bf16Params {
   const uint16_t* q;

@@ -6,17 +6,20 @@
 // Q/K/V); the close comment separates causal and non-causal shapes.
 //
 // Design (gfx950, wave64):
-//  * One workgroup = 4 waves = 128 query rows of one (sequence, head); each wave owns
-//    32 rows. Two workgroups share a CU, so each SIMD runs two waves from different
-//    workgroups and one's VALU work fills the other's MFMA time. Workgroups are ordered
-//    heaviest first: the flattened block index walks query tiles from the last (most
-//    keys under a causal mask) to the first, with heads and sequences fastest.
-//  * 64-key K tiles live in three rotating LDS buffers and FP8 V tiles in two, filled by
+//  * One workgroup = 8 waves = 256 query rows of one (sequence, head); each wave owns
+//    32 rows; one workgroup per CU, two waves per SIMD, so one wave's VALU work fills the
+//    other's MFMA time. Every K/V tile a workgroup loads and converts serves 256 rows
+//    (4-wave workgroups of 128 rows, two per CU, are a build option: 5 % slower on the
+//    32K causal prefill). Workgroups are ordered heaviest first: the flattened block
+//    index walks query tiles from the last (most keys under a causal mask) to the first,
+//    with heads and sequences fastest.
+//  * 64-key K tiles and FP8 V tiles live in two LDS buffers each, filled by
 //    global->LDS DMA (global_load_lds_dwordx4, no register staging). K rows are padded to
 //    208 bytes; V rows are 128 bytes with XOR-swizzled 16-byte chunks (see v_swizzle).
-//    Iteration t issues the loads of K(t+3) and V(t+1) and computes, interleaved, the PV
-//    MFMAs of tile t-1, the S MFMAs of tile t+1 and the softmax of tile t; after a
-//    barrier the waves convert V tile t to bf16 V^T for the next iteration's PV.
+//    Iteration t issues the loads of K(t+2) and V(t+1) at its start and computes,
+//    interleaved, the PV MFMAs of tile t-1, the S MFMAs of tile t+1, the softmax of tile
+//    t and the conversion of V tile t to bf16 V^T (two V^T buffers) for the next
+//    iteration's PV; one barrier per tile.
 //  * S^T = K * Q^T on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32): the Q fragment
 //    (32 rows x 192) stays in registers as the B operand, K rows are read from LDS as
 //    the A operand. In the 32x32 accumulator layout every lane holds one query row
@@ -31,13 +34,14 @@
 //    E4M3 P carries up to 2^-4 relative error per weight, more than the output tolerance
 //    allows on diffuse heads, and two E4M3 terms cost more VALU work than this path).
 //    Registers 8 ck .. 8 ck + 7 of an S accumulator are one P^T B operand (16 keys). V
-//    stays FP8 in HBM and LDS: each wave reads its 32-dim block of the tile with
+//    stays FP8 in HBM and LDS: the waves read 32-dim blocks of the tile with
 //    ds_read_b64_tr_b8 (within each 16-lane group, output lane i receives byte i % 8 of
 //    the 8-byte windows addressed by lanes 2b + i/8, so lane i gets dim d0 + i of 8 keys
-//    in the key order of the P operand), converts it exactly to bf16
-//    (v_cvt_scalef32_pk_bf16_fp8) and stores it as V^T rows; the keys a lane converts
+//    in the key order of the P operand), convert them exactly to bf16
+//    (v_cvt_scalef32_pk_bf16_fp8) and store them as V^T rows; the keys a lane converts
 //    are exactly those its own PV A operands need, so every A operand is one 16-byte
-//    read. The conversion is shared by the workgroup: 16 conversions per lane per tile.
+//    read. The conversion is shared by the workgroup: waves w and w + 4 convert the two
+//    key halves of dim block w % 4, 8 conversions per lane per tile.
 //  * Causal (bottom-right aligned: key j visible to row i iff j <= i + Lk - Lq):
 //    a wave skips tiles past its last visible key; only tiles that cross the
 //    diagonal or the ragged end are masked element-wise.
@@ -61,10 +65,11 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int kDqk = 192;
 constexpr int kDv = 128;
 #ifndef MLA_PREFILL_WAVES
-#define MLA_PREFILL_WAVES 4
+#define MLA_PREFILL_WAVES 8
 #endif
 constexpr int kWaves = MLA_PREFILL_WAVES;  // waves per workgroup
 constexpr int kWgPerCu = 8 / kWaves;       // resident workgroups per CU (2 waves per SIMD)
+static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves per workgroup");
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
@@ -365,7 +370,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   if (wave_tiles > 0) qk_tile(kbuf(0), col, g, qf, s_cur);
   block_barrier();  // K(0) is read: iteration 0 may load K(2) into its buffer
 
-  static_assert(kWaves == 4, "each wave converts one 32-dim block of V");
+  static_assert(kWaves == 4 || kWaves == 8, "the waves split the V conversion evenly");
+  // V conversion: wave w converts dim block w & 3; with 4 waves both key halves of it,
+  // with 8 waves the half w >> 2
+  const int conv_db = wave & 3;
   const v2bf ones2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
   // Softmax of 16 keys: S block b2, accumulator registers 8 ck .. 8 ck + 7. P = 2^(c*s +
   // nbias) rounded to bf16 (nearest even) is the B operand of one bf16 PV MFMA (MFMA
@@ -394,8 +402,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   // keys that lane (g, col) converts are exactly those its PV A operands need, so PV
   // operand (db, b2, ck) is the 16 bytes at 64 g + 32 b2 + 16 ck of row 32 db + col.
   auto convert_half = [&](int t, int half) {  // the keys of S block b2 = half
-    const uint8_t* vp = vbuf(t) + (vt_off ^ (wave << 5)) + 32 * half * kVStride;
-    uint8_t* dst = vtbuf(t) + (32 * wave + col) * kVtStride + 64 * g + 32 * half;
+    const uint8_t* vp = vbuf(t) + (vt_off ^ (conv_db << 5)) + 32 * half * kVStride;
+    uint8_t* dst = vtbuf(t) + (32 * conv_db + col) * kVtStride + 64 * g + 32 * half;
     const v2i r0 = read_tr8(vp);
     const v2i r1 = read_tr8(vp + 16 * kVStride);
     const int raw[4] = {r0.x, r0.y, r1.x, r1.y};
@@ -509,7 +517,11 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
           const int q = j >> 2;
           pb_c[q] = softmax_chunk(s_c, nbias, q >> 1, q & 1);
         }
-        if (convert && (j == 5 || j == 9)) convert_half(it, j == 9);
+        if constexpr (kWaves == 4) {
+          if (convert && (j == 5 || j == 9)) convert_half(it, j == 9);
+        } else {
+          if (convert && j == 5) convert_half(it, wave >> 2);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       s_n[1] = mfma_f8(ka, qf[2], s_n[1]);  // S MFMA 5
@@ -524,8 +536,12 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
           for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
     } else if (convert) {
-      convert_half(it, 0);
-      convert_half(it, 1);
+      if constexpr (kWaves == 4) {
+        convert_half(it, 0);
+        convert_half(it, 1);
+      } else {
+        convert_half(it, wave >> 2);
+      }
     }
     wait_vmcnt(0);  // K(it+2) and V(it+1) have landed
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // so have the V^T stores
