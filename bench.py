@@ -355,7 +355,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "dtype": "fp8_e4m3 Q/K/V (S on FP8 MFMA; P and decoded V on bf16 MFMA; fp32 accumulate)",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: {wl.description}",
