@@ -16,10 +16,11 @@
 //  * 64-key K tiles and FP8 V tiles live in two LDS buffers each, filled by
 //    global->LDS DMA (global_load_lds_dwordx4, no register staging). K rows are padded to
 //    208 bytes; V rows are 128 bytes with XOR-swizzled 16-byte chunks (see v_swizzle).
-//    Iteration t issues the loads of K(t+2) and V(t+1) at its start and computes,
-//    interleaved, the PV MFMAs of tile t-1, the S MFMAs of tile t+1, the softmax of tile
-//    t and the conversion of V tile t to bf16 V^T (two V^T buffers) for the next
-//    iteration's PV; one barrier per tile.
+//    Iteration t issues the loads of K(t+2) and V(t+1) at its start, then the S MFMAs of
+//    tile t+1 with the row max of tile t and the conversion of V tile t to bf16 V^T (two
+//    V^T buffers) between them, then the PV MFMAs of tile t-1 with the exponentials of
+//    tile t between them (exponentials co-issue with bf16 MFMAs, hardly with FP8 ones);
+//    one barrier per tile.
 //  * S^T = K * Q^T on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32): the Q fragment
 //    (32 rows x 192) stays in registers as the B operand, K rows are read from LDS as
 //    the A operand. In the 32x32 accumulator layout every lane holds one query row
@@ -375,25 +376,21 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   // with 8 waves the half w >> 2
   const int conv_db = wave & 3;
   const v2bf ones2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  // Softmax of 16 keys: S block b2, accumulator registers 8 ck .. 8 ck + 7. P = 2^(c*s +
-  // nbias) rounded to bf16 (nearest even) is the B operand of one bf16 PV MFMA (MFMA
-  // k-index 8 g + i stands for key 32 b2 + 16 ck + 8 (i / 4) + 4 g + i % 4); the row sum
-  // adds the rounded weights.
-  auto softmax_chunk = [&](const v16f(&sc)[2], float nbias, int b2, int ck) {
-    v8bf pb;
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[b2][8 * ck + i], c, nbias));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[b2][8 * ck + i + 1], c, nbias));
-      const v2bf pr = __builtin_convertvector(v2f{e0, e1}, v2bf);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l_run, false);
-      pb[i] = pr[0];
-      pb[i + 1] = pr[1];
-    }
-    // pin the chunk here: its result is only read in the next iteration, and the compiler
+  // Softmax of two keys: S block b2, accumulator registers 8 ck + 2 i and 8 ck + 2 i + 1.
+  // P = 2^(c*s + nbias) rounded to bf16 (nearest even) fills elements 2 i, 2 i + 1 of the
+  // B operand of one bf16 PV MFMA (registers 8 ck .. 8 ck + 7 of S block b2 make one
+  // operand: MFMA k-index 8 g + i stands for key 32 b2 + 16 ck + 8 (i / 4) + 4 g + i % 4);
+  // the row sum adds the rounded weights.
+  auto softmax_pair = [&](const v16f(&sc)[2], float nbias, int b2, int ck, int i, v8bf& pb) {
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[b2][8 * ck + 2 * i], c, nbias));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[b2][8 * ck + 2 * i + 1], c, nbias));
+    const v2bf pr = __builtin_convertvector(v2f{e0, e1}, v2bf);
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l_run, false);
+    pb[2 * i] = pr[0];
+    pb[2 * i + 1] = pr[1];
+    // pin the pair here: its result is only read in the next iteration, and the compiler
     // would otherwise sink it below the MFMAs it is meant to overlap
-    asm volatile("" ::"v"(pb), "v"(l_run));
-    return pb;
+    asm volatile("" ::"v"(pr), "v"(l_run));
   };
   // The transposed reads give lane (g, col) dim 32 db + col of the 32 keys
   // 32 b2 + 8 q + 4 g + i at byte 16 b2 + 4 q + i (b2, q, i = 0..1, 0..3, 0..3).
@@ -431,13 +428,14 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   // One software-pipelined iteration. S of tile it is in s_c, the bf16 P of tile it-1 in
   // pb_p and its V^T in V^T buffer (it-1) % 2 (on iteration 0: zero P and a zeroed
   // buffer). The iteration loads K(it+2) and V(it+1) into the buffers that K(it) and
-  // V(it-1) left at the previous barrier, and interleaves the 16 PV MFMAs of tile it-1,
-  // the 6 S MFMAs of tile it+1, the softmax of tile it (P to pb_c) and the conversion of
-  // V tile it to V^T buffer it % 2. LDS operands are read three PV MFMAs (V^T) or one S
-  // MFMA (K, three PV MFMAs earlier) ahead of use. A wave runs wave_tiles + 1 active
-  // iterations: the last one is a fully masked tile that only completes the PV of its
-  // last tile. Every wave takes part in every conversion. One barrier per iteration; all
-  // loads land before it.
+  // V(it-1) left at the previous barrier. It first issues the 6 S MFMAs of tile it+1 with
+  // the VALU work that needs no exponentials between them (mask, row max, rescale test,
+  // conversion of V tile it to V^T buffer it % 2), then the 16 PV MFMAs of tile it-1 with
+  // one softmax pair of tile it (P to pb_c) after each: exponentials overlap bf16 MFMAs
+  // well and FP8 MFMAs poorly. LDS operands are read three PV MFMAs (V^T) or one S MFMA
+  // (K) ahead of use. A wave runs wave_tiles + 1 active iterations: the last one is a
+  // fully masked tile that only completes the PV of its last tile. Every wave takes part
+  // in every conversion. One barrier per iteration; all loads land before it.
   auto step = [&](int it, v16f(&s_c)[2], v16f(&s_n)[2], const v8bf(&pb_p)[4], v8bf(&pb_c)[4]) {
     const bool active = it < wave_iters;
     const bool convert = it < n_tiles;
@@ -459,6 +457,11 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
       const int kt = it * kBN;
       const bool need_mask =
           it >= wave_tiles || (kt + kBN > Lk) || (causal && kt + kBN - 1 > wrow0 + off);
+      // S MFMA k writes accumulator k & 1 with Q fragment k >> 1; the first two start from 0
+      const v16f zero = {};
+      s_n[0] = mfma_f8(ka, qf[0], zero);
+      ka = k_operand(kl, 1);
+      __builtin_amdgcn_sched_barrier(0);
       if (need_mask) {
         // side-effect barrier: keeps this rare block a real branch (the compiler would
         // otherwise if-convert it into selects executed on every tile)
@@ -476,6 +479,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
         mx = vmax3(mx, vmax3(s_c[0][r], s_c[0][r + 1], s_c[1][r]), s_c[1][r + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      s_n[1] = mfma_f8(ka, qf[0], zero);
+      ka = k_operand(kl, 2);
+      __builtin_amdgcn_sched_barrier(0);
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                          false, false);
@@ -497,34 +504,37 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
       }
       const float nbias = (m_run == -INFINITY) ? 0.f : -m_run;
 
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s_n[b2][r] = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
+      s_n[0] = mfma_f8(ka, qf[1], s_n[0]);
+      ka = k_operand(kl, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      s_n[1] = mfma_f8(ka, qf[1], s_n[1]);
+      ka = k_operand(kl, 4);
+      __builtin_amdgcn_sched_barrier(0);
+      if (convert) {
+        if constexpr (kWaves == 4) {
+          convert_half(it, 0);
+          convert_half(it, 1);
+        } else {
+          convert_half(it, wave >> 2);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      s_n[0] = mfma_f8(ka, qf[2], s_n[0]);
+      ka = k_operand(kl, 5);
+      __builtin_amdgcn_sched_barrier(0);
+      s_n[1] = mfma_f8(ka, qf[2], s_n[1]);
+      __builtin_amdgcn_sched_barrier(0);
       // PV MFMA j covers dims 32 (j & 3) .. + 31 and key chunk q = j >> 2 (b2 = q >> 1,
-      // ck = q & 1); S MFMAs 0..4 follow PV MFMAs 1, 4, 7, 10, 13 and S MFMA 5 the last;
-      // softmax chunk q follows PV MFMA 4 q + 3, the conversion halves PV MFMAs 5 and 9
+      // ck = q & 1); softmax pair j & 3 of chunk q follows it
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         o[j & 3] = mfma_bf16(va[j % 3], pb_p[j >> 2], o[j & 3]);
         if (j + 3 < 16) va[j % 3] = vt_read(vt, (j + 3) & 3, (j + 3) >> 3, ((j + 3) >> 2) & 1);
-        if (j % 3 == 1) {  // S MFMA k = j / 3 (k = 0..4), then the operand of k + 1
-          const int k = j / 3;
-          s_n[k & 1] = mfma_f8(ka, qf[k >> 1], s_n[k & 1]);
-          ka = k_operand(kl, k + 1);
-        }
-        if ((j & 3) == 3) {
-          const int q = j >> 2;
-          pb_c[q] = softmax_chunk(s_c, nbias, q >> 1, q & 1);
-        }
-        if constexpr (kWaves == 4) {
-          if (convert && (j == 5 || j == 9)) convert_half(it, j == 9);
-        } else {
-          if (convert && j == 5) convert_half(it, wave >> 2);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        softmax_pair(s_c, nbias, j >> 3, (j >> 2) & 1, j & 3, pb_c[j >> 2]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      s_n[1] = mfma_f8(ka, qf[2], s_n[1]);  // S MFMA 5
 
       if (rescale) {
         // alpha passes through an opaque asm so that the multiplies stay in this rare
