@@ -398,12 +398,17 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   // 32 w + col, bytes 64 g .. 64 g + 63 hold the lane's 32 keys in the order above. The
   // keys that lane (g, col) converts are exactly those its PV A operands need, so PV
   // operand (db, b2, ck) is the 16 bytes at 64 g + 32 b2 + 16 ck of row 32 db + col.
-  auto convert_half = [&](int t, int half) {  // the keys of S block b2 = half
+  // The conversion in two parts, so that each fills a gap between FP8 MFMAs: the
+  // transposed reads of key half `half` (the keys of S block b2 = half), then the
+  // conversion and the two V^T stores.
+  auto conv_read = [&](int t, int half) {
     const uint8_t* vp = vbuf(t) + (vt_off ^ (conv_db << 5)) + 32 * half * kVStride;
-    uint8_t* dst = vtbuf(t) + (32 * conv_db + col) * kVtStride + 64 * g + 32 * half;
     const v2i r0 = read_tr8(vp);
     const v2i r1 = read_tr8(vp + 16 * kVStride);
-    const int raw[4] = {r0.x, r0.y, r1.x, r1.y};
+    return v4i{r0.x, r0.y, r1.x, r1.y};
+  };
+  auto conv_write = [&](int t, int half, const v4i& raw) {
+    uint8_t* dst = vtbuf(t) + (32 * conv_db + col) * kVtStride + 64 * g + 32 * half;
     uint32_t cv[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -415,6 +420,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     *reinterpret_cast<uint4*>(dst) = make_uint4(cv[0], cv[1], cv[2], cv[3]);
     *reinterpret_cast<uint4*>(dst + 16) = make_uint4(cv[4], cv[5], cv[6], cv[7]);
   };
+  auto convert_half = [&](int t, int half) { conv_write(t, half, conv_read(t, half)); };
   auto vt_read = [&](const uint8_t* vt, int db, int b2, int ck) {
     return *reinterpret_cast<const v8bf*>(vt + (32 * db + col) * kVtStride + 64 * g + 32 * b2 +
                                           16 * ck);
@@ -429,8 +435,9 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   // pb_p and its V^T in V^T buffer (it-1) % 2 (on iteration 0: zero P and a zeroed
   // buffer). The iteration loads K(it+2) and V(it+1) into the buffers that K(it) and
   // V(it-1) left at the previous barrier. It first issues the 6 S MFMAs of tile it+1 with
-  // the VALU work that needs no exponentials between them (mask, row max, rescale test,
-  // conversion of V tile it to V^T buffer it % 2), then the 16 PV MFMAs of tile it-1 with
+  // the VALU work that needs no exponentials spread between them (mask and row max of S
+  // block 0; row max of block 1; rescale test; transposed reads of V tile it; their
+  // conversion to V^T buffer it % 2), then the 16 PV MFMAs of tile it-1 with
   // one softmax pair of tile it (P to pb_c) after each: exponentials overlap bf16 MFMAs
   // well and FP8 MFMAs poorly. LDS operands are read three PV MFMAs (V^T) or one S MFMA
   // (K) ahead of use. A wave runs wave_tiles + 1 active iterations: the last one is a
@@ -475,13 +482,19 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
             if (all || key >= Lk || (causal && key > my_row + off)) s_c[b2][r] = -INFINITY;
           }
       }
+      // the row max of S block 0, S MFMA 1, that of block 1, S MFMA 2
       float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2)
-        mx = vmax3(mx, vmax3(s_c[0][r], s_c[0][r + 1], s_c[1][r]), s_c[1][r + 1]);
+      for (int r = 0; r < 16; r += 2) mx = vmax3(mx, s_c[0][r], s_c[0][r + 1]);
       __builtin_amdgcn_sched_barrier(0);
       s_n[1] = mfma_f8(ka, qf[0], zero);
       ka = k_operand(kl, 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = vmax3(mx, s_c[1][r], s_c[1][r + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      s_n[0] = mfma_f8(ka, qf[1], s_n[0]);
+      ka = k_operand(kl, 3);
       __builtin_amdgcn_sched_barrier(0);
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
@@ -504,24 +517,24 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
       }
       const float nbias = (m_run == -INFINITY) ? 0.f : -m_run;
 
-      __builtin_amdgcn_sched_barrier(0);
-      s_n[0] = mfma_f8(ka, qf[1], s_n[0]);
-      ka = k_operand(kl, 3);
+      // S MFMA 3, the transposed V reads, S MFMA 4, the conversion, S MFMA 5
       __builtin_amdgcn_sched_barrier(0);
       s_n[1] = mfma_f8(ka, qf[1], s_n[1]);
       ka = k_operand(kl, 4);
       __builtin_amdgcn_sched_barrier(0);
+      v4i craw0, craw1;
       if (convert) {
-        if constexpr (kWaves == 4) {
-          convert_half(it, 0);
-          convert_half(it, 1);
-        } else {
-          convert_half(it, wave >> 2);
-        }
+        craw0 = conv_read(it, kWaves == 4 ? 0 : wave >> 2);
+        if constexpr (kWaves == 4) craw1 = conv_read(it, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       s_n[0] = mfma_f8(ka, qf[2], s_n[0]);
       ka = k_operand(kl, 5);
+      __builtin_amdgcn_sched_barrier(0);
+      if (convert) {
+        conv_write(it, kWaves == 4 ? 0 : wave >> 2, craw0);
+        if constexpr (kWaves == 4) conv_write(it, 1, craw1);
+      }
       __builtin_amdgcn_sched_barrier(0);
       s_n[1] = mfma_f8(ka, qf[2], s_n[1]);
       __builtin_amdgcn_sched_barrier(0);
