@@ -83,7 +83,6 @@ constexpr int kVTile = kBN * kVStride;
 constexpr int kVtStride = 144;
 constexpr int kVtBytes = kDv * kVtStride;
 constexpr int kLdsBytes = 2 * (kKTile + kVTile + kVtBytes);  // 79872: two workgroups per CU
-constexpr int kKChunks = kBN * kDqk / 16;  // 768 16-byte chunks per K tile
 constexpr float kLn2 = 0.69314718055994530942f;
 // P = 2^(logit*log2e - m) <= 2^kRescaleSlack is a bf16 operand; the slack only bounds O.
 constexpr float kRescaleSlack = 8.0f;
