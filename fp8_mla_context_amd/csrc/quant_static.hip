@@ -49,42 +49,89 @@ __device__ __forceinline__ float descale_of_amax(float amax) {
   return fmaxf(__fdiv_rn(amax, 448.f), 0x1p-126f);
 }
 
-__global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantParams p) {
-  const uint32_t stride = gridDim.x * kQuantThreads;
-  for (uint32_t c = blockIdx.x * kQuantThreads + threadIdx.x; c < p.total_chunks; c += stride) {
-    int j = 0;
-    if (p.n_jobs > 1 && c >= p.job[1].chunk_begin) j = 1;
-    if (p.n_jobs > 2 && c >= p.job[2].chunk_begin) j = 2;
-    const QuantJobDev& jb = p.job[j];
-    const uint32_t local = c - jb.chunk_begin;
-    // chunks per (token, head) row: 12 for D = 192, 8 for D = 128
-    uint32_t row, col;
-    if (jb.head_dim == 192) {
-      row = local / 12u;
-      col = local - row * 12u;
-    } else {
-      row = local >> 3;
-      col = local & 7u;
-    }
-    const uint32_t t = mla::fdiv(row, p.heads);
-    const uint32_t h = row - t * p.heads.d;
-    const float d = jb.from_amax ? descale_of_amax(jb.descale[h]) : jb.descale[h];
-    const float r = 1.0f / d;
-    const uint16_t* src = jb.x + static_cast<int64_t>(t) * jb.stride_token +
-                          static_cast<int64_t>(h) * jb.stride_head + col * 16u;
-    uint32_t w[8];
-    if (jb.vec) {
-      const uint4 a = *reinterpret_cast<const uint4*>(src);
-      const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
-      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-      w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    } else {
+constexpr int kScaleSlots = 3 * 512;  // (job, head) descales and reciprocals staged in LDS
+
+// Chunk c of the launch: its 16 bf16 inputs in w (elements 2i, 2i+1 in w[i]), its
+// (job, head) slot and the address of its 16 codes.
+__device__ __forceinline__ void load_chunk(const QuantParams& p, uint32_t c, uint32_t (&w)[8],
+                                           uint32_t& slot, uint8_t*& dst) {
+  int j = 0;
+  if (p.n_jobs > 1 && c >= p.job[1].chunk_begin) j = 1;
+  if (p.n_jobs > 2 && c >= p.job[2].chunk_begin) j = 2;
+  const QuantJobDev& jb = p.job[j];
+  const uint32_t local = c - jb.chunk_begin;
+  uint32_t row, col;
+  if (jb.head_dim == 192) {
+    row = local / 12u;
+    col = local - row * 12u;
+  } else {
+    row = local >> 3;
+    col = local & 7u;
+  }
+  const uint32_t t = mla::fdiv(row, p.heads);
+  const uint32_t h = row - t * p.heads.d;
+  slot = j * p.heads.d + h;
+  const uint16_t* src = jb.x + static_cast<int64_t>(t) * jb.stride_token +
+                        static_cast<int64_t>(h) * jb.stride_head + col * 16u;
+  if (jb.vec) {
+    const uint4 a = *reinterpret_cast<const uint4*>(src);
+    const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        w[i] = static_cast<uint32_t>(src[2 * i]) | (static_cast<uint32_t>(src[2 * i + 1]) << 16);
+    for (int i = 0; i < 8; ++i)
+      w[i] = static_cast<uint32_t>(src[2 * i]) | (static_cast<uint32_t>(src[2 * i + 1]) << 16);
+  }
+  dst = jb.y + static_cast<int64_t>(row) * jb.head_dim + col * 16u;
+}
+
+// Each (job, head) descale and its reciprocal are formed once per workgroup in LDS (from
+// the amax for the dynamic path); heads beyond the LDS table read them per chunk.
+__global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantParams p) {
+  __shared__ float2 sc[kScaleSlots];  // (descale, 1 / descale) per (job, head)
+  const int H = static_cast<int>(p.heads.d);
+  const int slots = p.n_jobs * H;
+  const bool use_lds = slots <= kScaleSlots;
+  if (use_lds) {
+    for (int i = threadIdx.x; i < slots; i += kQuantThreads) {
+      const QuantJobDev& jb = p.job[i / H];
+      const float d = jb.from_amax ? descale_of_amax(jb.descale[i % H]) : jb.descale[i % H];
+      sc[i] = make_float2(d, 1.0f / d);
     }
-    const uint4 o = mla::dev::quant16(w, d, r);
-    *reinterpret_cast<uint4*>(jb.y + static_cast<int64_t>(row) * jb.head_dim + col * 16u) = o;
+  }
+  __syncthreads();
+  const uint32_t stride = gridDim.x * kQuantThreads;
+  uint32_t c = blockIdx.x * kQuantThreads + threadIdx.x;
+  // two chunks per iteration: both chunks' loads are in flight before either is rounded
+  for (; c + stride < p.total_chunks; c += 2 * stride) {
+    uint32_t w0[8], w1[8], s0, s1;
+    uint8_t *d0, *d1;
+    load_chunk(p, c, w0, s0, d0);
+    load_chunk(p, c + stride, w1, s1, d1);
+    float2 a0, a1;
+    if (use_lds) { a0 = sc[s0]; a1 = sc[s1]; }
+    else {
+      const int j0 = s0 / H, j1 = s1 / H;
+      const float e0 = p.job[j0].from_amax ? descale_of_amax(p.job[j0].descale[s0 % H]) : p.job[j0].descale[s0 % H];
+      const float e1 = p.job[j1].from_amax ? descale_of_amax(p.job[j1].descale[s1 % H]) : p.job[j1].descale[s1 % H];
+      a0 = make_float2(e0, 1.0f / e0); a1 = make_float2(e1, 1.0f / e1);
+    }
+    *reinterpret_cast<uint4*>(d0) = mla::dev::quant16(w0, a0.x, a0.y);
+    *reinterpret_cast<uint4*>(d1) = mla::dev::quant16(w1, a1.x, a1.y);
+  }
+  for (; c < p.total_chunks; c += stride) {
+    uint32_t w[8], s0;
+    uint8_t* d0;
+    load_chunk(p, c, w, s0, d0);
+    float2 a;
+    if (use_lds) a = sc[s0];
+    else {
+      const int j0 = s0 / H;
+      const float e0 = p.job[j0].from_amax ? descale_of_amax(p.job[j0].descale[s0 % H]) : p.job[j0].descale[s0 % H];
+      a = make_float2(e0, 1.0f / e0);
+    }
+    *reinterpret_cast<uint4*>(d0) = mla::dev::quant16(w, a.x, a.y);
   }
 }
 
