@@ -101,7 +101,14 @@ __global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantParams
     }
   }
   __syncthreads();
-  const uint32_t stride = gridDim.x * kQuantThreads;
+  // (descale, reciprocal) of a (job, head) slot
+  auto scale_of = [&](uint32_t slot) {
+    if (use_lds) return sc[slot];
+    const QuantJobDev& jb = p.job[slot / H];
+    const float d = jb.from_amax ? descale_of_amax(jb.descale[slot % H]) : jb.descale[slot % H];
+    return make_float2(d, 1.0f / d);
+  };
+  const uint32_t stride = gridDim.x * kQuantThreads;  // total_chunks < 2^31: no wrap below
   uint32_t c = blockIdx.x * kQuantThreads + threadIdx.x;
   // two chunks per iteration: both chunks' loads are in flight before either is rounded
   for (; c + stride < p.total_chunks; c += 2 * stride) {
@@ -109,14 +116,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantParams
     uint8_t *d0, *d1;
     load_chunk(p, c, w0, s0, d0);
     load_chunk(p, c + stride, w1, s1, d1);
-    float2 a0, a1;
-    if (use_lds) { a0 = sc[s0]; a1 = sc[s1]; }
-    else {
-      const int j0 = s0 / H, j1 = s1 / H;
-      const float e0 = p.job[j0].from_amax ? descale_of_amax(p.job[j0].descale[s0 % H]) : p.job[j0].descale[s0 % H];
-      const float e1 = p.job[j1].from_amax ? descale_of_amax(p.job[j1].descale[s1 % H]) : p.job[j1].descale[s1 % H];
-      a0 = make_float2(e0, 1.0f / e0); a1 = make_float2(e1, 1.0f / e1);
-    }
+    const float2 a0 = scale_of(s0), a1 = scale_of(s1);
     *reinterpret_cast<uint4*>(d0) = mla::dev::quant16(w0, a0.x, a0.y);
     *reinterpret_cast<uint4*>(d1) = mla::dev::quant16(w1, a1.x, a1.y);
   }
@@ -124,13 +124,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantParams
     uint32_t w[8], s0;
     uint8_t* d0;
     load_chunk(p, c, w, s0, d0);
-    float2 a;
-    if (use_lds) a = sc[s0];
-    else {
-      const int j0 = s0 / H;
-      const float e0 = p.job[j0].from_amax ? descale_of_amax(p.job[j0].descale[s0 % H]) : p.job[j0].descale[s0 % H];
-      a = make_float2(e0, 1.0f / e0);
-    }
+    const float2 a = scale_of(s0);
     *reinterpret_cast<uint4*>(d0) = mla::dev::quant16(w, a.x, a.y);
   }
 }
