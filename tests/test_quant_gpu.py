@@ -93,3 +93,25 @@ def test_zero_tokens_is_noop(gpu_lib):
     assert y.shape == (0, 12, 192)
     a = B.amax_per_head(x)
     assert np.array_equal(host(a), np.zeros(12, np.float32))
+
+
+def test_many_heads_scale_lookup_without_lds_table(gpu_lib):
+    """More (tensor, head) slots (3 x 1100) than the quantizer's descale table and the amax
+    kernel's maxima hold in LDS: both then read and update memory per chunk; codes and
+    descales stay bit-exact, for the static and the dynamic path."""
+    B = gpu_lib
+    rng = np.random.default_rng(7)
+    T, H = 5, 1100
+    xs, ds = [], []
+    for dim in (192, 192, 128):
+        z = (rng.standard_normal((T, H, dim)) * 4).astype(np.float32)
+        xs.append(((z.view(np.uint32) + 0x8000) >> 16).astype(np.uint16))
+        ds.append(np.exp2(rng.uniform(-9, 1, H)).astype(np.float32))
+    got = B.quant_static([dev_bf16(x) for x in xs], [dev(d) for d in ds])
+    for g, x, d in zip(got, xs, ds):
+        assert np.array_equal(host(g), oracle.quant_static(x, d))
+    codes, d_gpu = B.quant_dynamic([dev_bf16(x) for x in xs])
+    for i, (g, x) in enumerate(zip(codes, xs)):
+        c_ref, d_ref = oracle.quant_dynamic(x)
+        assert np.array_equal(host(d_gpu[i]), d_ref)
+        assert np.array_equal(host(g), c_ref)
