@@ -1,8 +1,8 @@
 """GPU parity of the FP8 varlen prefill against the fp64 oracle.
 
-Element-wise on small shapes that span several 128-row query tiles and
+Element-wise on small shapes that span several 256-row query tiles and
 64-key tiles with ragged tails (causal and non-causal, Lq != Lk both ways,
-empty sequences); the full small workloads; sampled rows of the 32K-token
+empty sequences, sequences without keys, both block orders); the full small workloads; sampled rows of the 32K-token
 causal workload in the launch configuration the benchmark times; and GPU-side
 invariants (run-to-run bitwise determinism, permutation of packed sequences,
 exact power-of-two V scaling, V = ones).
@@ -46,18 +46,25 @@ def _check(B, wl, causal=None, label=""):
 
 
 CASES = [
-    ("ragged_causal", [1, 5, 127, 128, 129, 300, 64, 0], None, True),
-    ("ragged_noncausal", [1, 5, 127, 128, 129, 300, 64, 0], None, False),
-    ("lk_gt_lq_causal", [100, 37, 200, 256], [300, 37, 64, 700], True),
-    ("lk_gt_lq_noncausal", [100, 37, 200, 256], [300, 37, 64, 700], False),
-    ("single_long", [777], None, True),
+    ("ragged_causal", [1, 5, 127, 128, 129, 300, 64, 0], None, True, 12),
+    ("ragged_noncausal", [1, 5, 127, 128, 129, 300, 64, 0], None, False, 12),
+    ("lk_gt_lq_causal", [100, 37, 200, 256], [300, 37, 64, 700], True, 12),
+    ("lk_gt_lq_noncausal", [100, 37, 200, 256], [300, 37, 64, 700], False, 12),
+    ("single_long", [777], None, True, 12),
+    # more queries than keys: bottom-right causal rows before the first key see nothing,
+    # and a sequence without keys leaves all its rows empty (zero output, LSE -inf)
+    ("lq_gt_lk_causal", [300, 129, 64, 5], [100, 0, 64, 3], True, 12),
+    ("lq_gt_lk_noncausal", [300, 129, 64, 5], [100, 0, 64, 3], False, 12),
+    # one sequence with a head count that is not a multiple of 4 and an odd number of
+    # query tiles: the plain heaviest-first block order instead of the XCD-aware one
+    ("one_seq_5_heads_odd_tiles", [600], None, True, 5),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(CASES)), ids=[c[0] for c in CASES])
 def test_prefill_small_cases(gpu_lib, case):
-    name, lq, lk, causal = CASES[case]
-    wl = make_random(100 + case, lq, lk, causal=causal, outliers=True)
+    name, lq, lk, causal, heads = CASES[case]
+    wl = make_random(100 + case, lq, lk, causal=causal, heads=heads, outliers=True)
     _check(gpu_lib, wl, label=name)
 
 
