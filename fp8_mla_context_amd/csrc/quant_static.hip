@@ -207,9 +207,12 @@ __global__ __launch_bounds__(kQuantThreads) void descale_of_amax_kernel(float* v
   if (i < n) v[i] = descale_of_amax(v[i]);
 }
 
-int grid_for(uint64_t work_items, int per_block) {
+// Grid of a grid-stride launch: at most blocks_per_cu blocks of 256 threads per CU (256
+// CUs). The quantizer takes 32 (measured 3-4 % faster than 16 on the 32K workload: more
+// loads in flight); the amax reduction 16 (one global atomic per head and workgroup).
+int grid_for(uint64_t work_items, int per_block, int blocks_per_cu) {
   uint64_t blocks = (work_items + per_block - 1) / per_block;
-  const uint64_t cap = 256ull * 16ull;  // 256 CUs x 16 resident blocks of 256 threads
+  const uint64_t cap = 256ull * static_cast<uint64_t>(blocks_per_cu);
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   return static_cast<int>(blocks);
@@ -270,8 +273,8 @@ int launch_amax(const QuantParams& p, uint64_t total, uint32_t* amax_bits, int n
                      dim3(kQuantThreads), 0, st, amax_bits, n);
   int s = mla::check_launch("zero_words_kernel");
   if (s != MLA_OK || total == 0) return s;
-  hipLaunchKernelGGL(amax_chunks_kernel, dim3(grid_for(total, kQuantThreads)), dim3(kQuantThreads),
-                     0, st, p, amax_bits);
+  hipLaunchKernelGGL(amax_chunks_kernel, dim3(grid_for(total, kQuantThreads, 16)),
+                     dim3(kQuantThreads), 0, st, p, amax_bits);
   return mla::check_launch("amax_chunks_kernel");
 }
 
@@ -284,7 +287,7 @@ extern "C" int mla_fp8_quant_static(const mla_quant_job* jobs, int32_t n_jobs, i
   const int st = build_params(jobs, n_jobs, n_heads, true, true, p, total);
   if (st != MLA_OK) return st;
   if (total == 0) return mla::ok();
-  hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(total, kQuantThreads)),
+  hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(total, kQuantThreads, 32)),
                      dim3(kQuantThreads), 0, static_cast<hipStream_t>(stream), p);
   return mla::check_launch("quant_static_kernel");
 }
@@ -308,7 +311,7 @@ extern "C" int mla_fp8_quant_dynamic(const mla_quant_job* jobs, int32_t n_jobs, 
       p.job[j].descale = descale_out + static_cast<int64_t>(j) * n_heads;
       p.job[j].from_amax = 1;
     }
-    hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(total, kQuantThreads)),
+    hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(total, kQuantThreads, 32)),
                        dim3(kQuantThreads), 0, hs, p);
     st = mla::check_launch("quant_static_kernel");
     if (st != MLA_OK) return st;
