@@ -79,7 +79,10 @@ def _gpu_codes(B, wl):
 @pytest.mark.gpu
 @pytest.mark.parametrize("lq,lk,seg,causal", [(300, 1000, 128, True), (257, 257, 64, True),
                                               (100, 700, 200, False), (130, 130, 1000, True),
-                                              (77, 0, 32, False)])
+                                              (77, 0, 32, False),
+                                              # 63 context segments + the diagonal: the most
+                                              # parts one query chunk can have
+                                              (64, 4096, 64, True)])
 def test_chunked_small_elementwise(gpu_lib, lq, lk, seg, causal):
     from tests.gpu_helpers import host
 

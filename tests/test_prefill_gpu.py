@@ -58,6 +58,9 @@ CASES = [
     # one sequence with a head count that is not a multiple of 4 and an odd number of
     # query tiles: the plain heaviest-first block order instead of the XCD-aware one
     ("one_seq_5_heads_odd_tiles", [600], None, True, 5),
+    # the XCD-aware order with 4 half-heads per XCD, and a single head
+    ("one_seq_16_heads", [1024], None, True, 16),
+    ("one_head_lk_gt_lq", [700], [900], True, 1),
 ]
 
 
