@@ -5,8 +5,11 @@ Element-wise on small shapes that span several 256-row query tiles and
 empty sequences, sequences without keys, both block orders); the full small workloads; sampled rows of the 32K-token
 causal workload in the launch configuration the benchmark times; and GPU-side
 invariants (run-to-run bitwise determinism, permutation of packed sequences,
-exact power-of-two V scaling, V = ones).
+exact power-of-two V scaling, V = ones); a lazy rescale forced on every tile and
+extreme softmax scales.
 """
+
+import dataclasses
 
 import numpy as np
 import pytest
@@ -161,3 +164,53 @@ def test_v_ones(gpu_lib):
     ds[2] = np.ones_like(ds[2])
     out, lse = _run_codes(B, wl, codes, ds)
     assert np.max(np.abs(out - 1.0)) <= 4e-3
+
+
+def _check_own_scales(B, wl, label, max_abs_gate=True):
+    # descales from the data itself (the tensors below are reshaped after generation)
+    ds = [oracle.descale_from_amax(oracle.amax_per_head(x)) for x in (wl.q, wl.k, wl.v)]
+    codes = oracle_codes(wl, ds)
+    out, lse = _run_codes(B, wl, codes, ds)
+    ref_o, ref_l = oracle_attention(wl, codes, ds)
+    errs = attention_errors(out, ref_o, lse, ref_l, sigma_v(wl),
+                            logit_scale(codes[0], codes[1], ds[0], ds[1], wl.softmax_scale))
+    print(label, errs, flush=True)
+    if not max_abs_gate:
+        errs = dict(errs, max_abs_sigma=0.0)
+    assert_attention_parity(errs, label)
+
+
+def test_rescale_on_every_tile(gpu_lib):
+    """Logits that grow by ~12 (base 2) per 64-key tile along the keys: every row's running
+    maximum moves past the lazy-rescale slack on every tile it sees, so O and the row sum
+    are rescaled on each iteration."""
+    from synth.inputs import bf16_bits_to_f32, f32_to_bf16_bits
+
+    wl = make_random(4242, [300, 517], None, causal=True)
+    q = bf16_bits_to_f32(wl.q)
+    k = bf16_bits_to_f32(wl.k)
+    q[:, :, 0] = 4.0
+    step = 12.0 / (np.log2(np.e) * wl.softmax_scale * 4.0)  # key-dim-0 rise per 64 keys
+    for b in range(wl.batch):
+        k0, k1 = int(wl.cu_seqlens_k[b]), int(wl.cu_seqlens_k[b + 1])
+        k[k0:k1, :, 0] = (step * np.arange(k1 - k0) / 64.0)[:, None]
+    wl = dataclasses.replace(wl, q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k))
+    _check_own_scales(gpu_lib, wl, "rescale every tile")
+
+
+@pytest.mark.parametrize("scale", [0.25, 1e-3])
+def test_softmax_scales(gpu_lib, scale):
+    """A softmax scale 3.5x the workloads' 1/sqrt(192) (sharper weights, larger logits) and
+    a tiny one (near-uniform weights), under the workloads' gates."""
+    wl = make_random(4343, [129, 700], [300, 700], causal=True, outliers=True)
+    _check_own_scales(gpu_lib, dataclasses.replace(wl, softmax_scale=scale), f"scale {scale}")
+
+
+def test_large_softmax_scale_rel_rms_and_lse(gpu_lib):
+    """Softmax scale 1.0 (14x the workloads'): near one-hot weights pass the FP8 MFMA's
+    logit error (about 2^-16 of sum |q_d k_d|, which grows with the scale) to single
+    outputs, so the element-wise max-abs gate stated for the workloads' scale is not
+    applied; rel-RMS and the LSE gate (which scales with the logit magnitude) are."""
+    wl = make_random(4343, [129, 700], [300, 700], causal=True, outliers=True)
+    _check_own_scales(gpu_lib, dataclasses.replace(wl, softmax_scale=1.0), "scale 1.0",
+                      max_abs_gate=False)
