@@ -16,7 +16,10 @@
 //   * non-causal requests split every query chunk over all key segments.
 // The host walks the plan: each query chunk's parts run as ONE prefill launch over
 // all its segments (a segment table in the kernel arguments), then one merge, on
-// the caller's stream. Partials are kept in fp32 in a caller-provided
+// the caller's stream. Adjacent non-causal segments of a query chunk are attended as
+// one range when the launch keeps at least four workgroups per CU that way (the LSE
+// merge is associative, so this equals merging their partials): fewer fp32 partials are
+// written and merged, and the workspace the plan needs is an upper bound. Partials are kept in fp32 in a caller-provided
 // workspace, so the output is rounded to bf16 once, by the merge; a query
 // chunk with a single part is written straight into `out`.
 #include <vector>
@@ -27,6 +30,10 @@ namespace {
 
 constexpr int kMaxParts = 64;  // the merge kernel's segment limit
 constexpr int64_t kAlign = 256;
+// Launch size below which adjacent non-causal segments stay separate: four workgroups
+// per CU of a 256-CU MI355X, with the prefill's default 256 query rows per workgroup.
+constexpr int64_t kMinBlocks = 4 * 256;
+constexpr int64_t kPrefillRows = 256;
 
 struct Part {
   int64_t k0, k1;
@@ -51,6 +58,26 @@ bool chunk_parts(int64_t lq, int64_t lk, int64_t seg, int32_t causal, int64_t r0
     parts.push_back({off + c0, off + std::min(r0, c0 + seg), 0});
   parts.push_back({off + r0, off + r1, 1});
   return true;
+}
+
+// Coalesce the leading n_nc non-causal parts (contiguous key ranges) into as few groups
+// of near-equal size as keep (groups + other parts) x blocks_per_part >= kMinBlocks.
+void group_parts(std::vector<Part>& parts, int64_t blocks_per_part) {
+  const int64_t n = static_cast<int64_t>(parts.size());
+  int64_t n_nc = 0;
+  while (n_nc < n && !parts[n_nc].causal) ++n_nc;
+  if (n_nc < 2) return;
+  int64_t ng = 1;
+  while (ng < n_nc && (ng + n - n_nc) * blocks_per_part < kMinBlocks) ++ng;
+  if (ng == n_nc) return;
+  std::vector<Part> out;
+  for (int64_t gi = 0, i = 0; gi < ng; ++gi) {
+    const int64_t cnt = n_nc / ng + (gi < n_nc % ng ? 1 : 0);
+    out.push_back({parts[i].k0, parts[i + cnt - 1].k1, 0});
+    i += cnt;
+  }
+  for (int64_t i = n_nc; i < n; ++i) out.push_back(parts[i]);
+  parts.swap(out);
 }
 
 int64_t max_parts(int64_t lq, int64_t lk, int64_t seg, int32_t causal) {
@@ -131,6 +158,7 @@ extern "C" int mla_fp8_prefill_chunked(const void* q, const void* k, const void*
     const int64_t rows = r1 - r0;
     if (!chunk_parts(lq, lk, seg, causal, r0, r1, parts))
       return mla::fail(MLA_ERR_INVALID_ARGUMENT, "no chunk plan");
+    group_parts(parts, (rows + kPrefillRows - 1) / kPrefillRows * n_heads);
     const int n = static_cast<int>(parts.size());
     if (n == 1) {
       // a single part is written straight into the output rows

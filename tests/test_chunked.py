@@ -3,8 +3,9 @@
 CPU: workspace sizing agrees with an independent count of the segment plan,
 and invalid requests fail before any HIP call.
 GPU: parity with the oracle's unsegmented attention on small ragged plans
-(element-wise), on the 4K-new-over-64K-cached workload at full size (sampled
-rows) and on the 128K-token workload processed in 16K segments (sampled rows).
+(element-wise), on plans whose adjacent segments the driver attends in groups,
+on the 4K-new-over-64K-cached workload at full size (sampled rows) and on the
+128K-token workload processed in 16K segments (sampled rows).
 """
 
 import math
@@ -98,6 +99,28 @@ def test_chunked_small_elementwise(gpu_lib, lq, lk, seg, causal):
                             sigma_v(wl), logit_scale(c_np[0], c_np[1], ds[0], ds[1], wl.softmax_scale))
     print((lq, lk, seg, causal), errs, flush=True)
     assert_attention_parity(errs, f"chunked {(lq, lk, seg, causal)}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunked_grouped_segments(gpu_lib, causal):
+    """128 heads make each part of a 64-row query chunk 128 workgroups, so the driver
+    attends the 15 (16) adjacent non-causal segments in 7 (8) uneven (even) groups."""
+    from tests.gpu_helpers import host
+
+    B = gpu_lib
+    lq, lk, seg = 64, 1024, 64
+    wl = make_random(991 + causal, [lq], [lk], causal=causal, heads=128, outliers=True)
+    ds, codes, dds = _gpu_codes(B, wl)
+    out, lse = B.prefill_chunked(codes[0], codes[1], codes[2], dds[0], dds[1], dds[2],
+                                 wl.softmax_scale, seg, causal)
+    c_np = [host(c) for c in codes]
+    ref_o, ref_l = oracle.attention_varlen(*c_np, wl.cu_seqlens_q, wl.cu_seqlens_k, *ds,
+                                           wl.softmax_scale, causal)
+    errs = attention_errors(bf16_bits_to_f64(host(out)), ref_o, host(lse).astype(np.float64), ref_l,
+                            sigma_v(wl), logit_scale(c_np[0], c_np[1], ds[0], ds[1], wl.softmax_scale))
+    print("grouped", causal, errs, flush=True)
+    assert_attention_parity(errs, f"chunked grouped causal={causal}")
 
 
 def _sampled_check(B, name, n_rows, label):
