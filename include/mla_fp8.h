@@ -260,8 +260,10 @@ int mla_merge_lse(int32_t n_segments, const void* const* outs, const float* cons
  * queries in chunks of seg_len rows; cached keys [0, Lk - Lq) in segments of
  * seg_len, seen in full by every query; for query chunk [r0, r1) the own keys
  * [Lk-Lq, Lk-Lq+r0) in segments of seg_len seen in full, then the diagonal
- * [Lk-Lq+r0, Lk-Lq+r1) as a causal call. Partials stay in fp32 (workspace) and
- * the merged output is rounded to bf16 once. The result equals
+ * [Lk-Lq+r0, Lk-Lq+r1) as a causal call. Adjacent non-causal segments of a query
+ * chunk are attended as one range when the launch keeps at least four workgroups
+ * per CU that way (the merge is associative). Partials stay in fp32 (workspace)
+ * and the merged output is rounded to bf16 once. The result equals
  * mla_fp8_prefill_varlen on the whole sequence up to rounding.
  *
  *   q, k, v     device E4M3, contiguous [Lq, H, 192], [Lk, H, 192], [Lk, H, 128]
