@@ -131,7 +131,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(heads or context segments would shard with no or one exchange step).",
               file=sys.stderr)
         return 2
