@@ -4,8 +4,10 @@
 One step = the whole hot path over one batch of synthetic input that is already
 resident in HBM. For the default 32K-token causal workload (C3, a single segment)
 that is the one-launch static quantizer over Q, K and V, then the FP8 varlen
-prefill. For the chunked workloads (C4, C5) it is the quantizer, then the chunked
-prefill (one prefill launch per (query chunk, context segment) and the LSE merges).
+prefill; likewise for C1 (128 tokens), C2 (8 packed sequences) and NC (4096
+queries over 65536 context keys, non-causal). For the chunked workloads (C4, C5) it
+is the quantizer, then the chunked prefill (one prefill launch per query chunk over
+its context segments, with the LSE merges).
 The headline value is causal-counted TFLOP/s of the step: 640 FLOP per visible
 (query, key) pair and head, with 640 = 2 * (192 + 128).
 
@@ -89,17 +91,78 @@ def cpu_baseline(wl, codes_np, ds, target_s: float, seed: int = 1):
     for frac in (1.0 / 3.0, 1.0):
         n_rows = int(min(wl.total_q, max(n_rows, n_rows * frac * target_s / max(dt, 1e-3))))
         rows, dt = run(n_rows)
-    # visible keys of each sampled row (one sequence: the last Lq of Lk tokens)
-    lq, lk = wl.total_q, wl.total_k
-    vis = np.minimum(lk, rows + (lk - lq) + 1) if wl.causal else np.full(n_rows, lk)
+    # visible keys of each sampled row (its sequence's last Lq of Lk tokens)
+    cu_q = wl.cu_seqlens_q.astype(np.int64)
+    cu_k = wl.cu_seqlens_k.astype(np.int64)
+    seq = np.searchsorted(cu_q, rows, side="right") - 1
+    lq = cu_q[seq + 1] - cu_q[seq]
+    lk = cu_k[seq + 1] - cu_k[seq]
+    local = rows - cu_q[seq]
+    vis = np.clip(local + (lk - lq) + 1, 0, lk) if wl.causal else lk
     flop = float(np.sum(vis)) * wl.q.shape[1] * FLOP_PER_PAIR
+    try:
+        host_cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        host_cores = os.cpu_count()
     return {
-        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        "blas_threads": int(threads), "host_cores": int(host_cores), "kind": "oracle",
         "sample": f"{n_rows} seeded query rows x {wl.q.shape[1]} heads of {wl.name} "
                   f"({float(np.sum(vis)):.3g} visible pairs per head), fp64 NumPy oracle "
                   f"attention on the dequantized FP8 inputs, {dt:.1f} s",
         "seconds": dt,
     }
+
+
+def public_plan(torch, B, codes, descales, softmax_scale, seg, lq, lk, out, lse):
+    """The segmented plan of one causal sequence (the last lq of lk tokens) through the public
+    calls only, without grouping: per query chunk of seg rows, one prefill_varlen per
+    context segment of seg keys (non-causal) and one for the diagonal (causal), each into
+    its own bf16 partial and LSE, then merge_lse over the chunk's partials. Returns a
+    closure that runs the plan and the number of prefill and merge launches."""
+    heads = codes[0].shape[1]
+    off = lk - lq
+    plan = []
+    for r0 in range(0, lq, seg):
+        r1 = min(lq, r0 + seg)
+        parts = [(k0, min(off, k0 + seg), False) for k0 in range(0, off, seg)]
+        parts += [(off + c0, off + min(r0, c0 + seg), False) for c0 in range(0, r0, seg)]
+        parts.append((off + r0, off + r1, True))
+        plan.append((r0, r1, parts))
+    n_max = max(len(p) for _, _, p in plan)
+    rows_max = min(seg, lq)
+    pouts = [torch.empty((rows_max, heads, 128), dtype=torch.bfloat16, device="cuda")
+             for _ in range(n_max)]
+    plses = [torch.empty((heads, rows_max), dtype=torch.float32, device="cuda")
+             for _ in range(n_max)]
+    cu = {}
+
+    def cu_of(n):
+        if n not in cu:
+            cu[n] = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+        return cu[n]
+
+    def run():
+        for r0, r1, parts in plan:
+            rows = r1 - r0
+            q = codes[0][r0:r1]
+            if len(parts) == 1:
+                k0, k1, causal = parts[0]
+                B.prefill_varlen(q, codes[1][k0:k1], codes[2][k0:k1], cu_of(rows), cu_of(k1 - k0),
+                                 rows, k1 - k0, *descales, softmax_scale, causal,
+                                 out=out[r0:r1], lse=lse[:, r0:r1])
+                continue
+            for i, (k0, k1, causal) in enumerate(parts):
+                B.prefill_varlen(q, codes[1][k0:k1], codes[2][k0:k1], cu_of(rows), cu_of(k1 - k0),
+                                 rows, k1 - k0, *descales, softmax_scale, causal,
+                                 out=pouts[i][:rows], lse=plses[i][:, :rows])
+            n = len(parts)
+            B.merge_lse([p[:rows] for p in pouts[:n]], [p[:, :rows] for p in plses[:n]],
+                        out=out[r0:r1], lse_out=lse[:, r0:r1])
+
+    n_prefill = sum(len(p) for _, _, p in plan)
+    n_merge = sum(1 for _, _, p in plan if len(p) > 1)
+    return run, n_prefill, n_merge
 
 
 def event_ms(torch, fn, reps: int, stream):
@@ -121,7 +184,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="C3", choices=["C3", "C4", "C5"])
+    ap.add_argument("--workload", default="C3", choices=["C1", "C2", "C3", "C4", "C5", "NC"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the timed oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -247,6 +310,20 @@ def main(argv=None):
         single_ms, _ = event_ms(torch, prefill_single, reps, stream)
         kernels["unsegmented_prefill_ms"] = round(single_ms, 4)
         kernels["unsegmented_TFLOPs"] = round(flop / (single_ms * 1e-3) / 1e12, 2)
+        # the plan as the workload states it (every context segment its own call, bf16
+        # partials, one public merge per query chunk), through the public calls
+        p_out = torch.empty_like(out)
+        p_lse = torch.empty_like(lse)
+        run_plan, n_pf, n_mg = public_plan(torch, B, codes, descales, wl.softmax_scale,
+                                           wl.segment_len, wl.total_q, wl.total_k, p_out, p_lse)
+        run_plan()
+        plan_ms, _ = event_ms(torch, run_plan, max(3, reps // 4), stream)
+        kernels["public_segment_plan"] = {
+            "ms": round(plan_ms, 4), "TFLOPs": round(flop / (plan_ms * 1e-3) / 1e12, 2),
+            "prefill_launches": n_pf, "merge_launches": n_mg}
+        del p_out, p_lse
+        log(f"[bench] as-specified segment plan through the public calls ({n_pf} prefill + "
+            f"{n_mg} merge launches): {plan_ms:.3f} ms = {flop / (plan_ms * 1e-3) / 1e12:.1f} TFLOP/s")
         # the public merge on as many bf16 partials as the last query chunk combines
         seg = wl.segment_len
         n_parts = min(64, (wl.total_k + seg - 1) // seg)
@@ -267,6 +344,12 @@ def main(argv=None):
             f"{rows} rows: {merge_ms * 1e3:.1f} us ({merge_bytes / merge_ms / 1e6:.0f} GB/s)")
     else:
         kernels["prefill_ms"] = round(prefill_ms, 4)
+        # the varlen grid: query tiles of the longest sequence x sequences x heads; the
+        # workgroups of shorter sequences past their last row exit at once
+        lens = np.diff(wl.cu_seqlens_q)
+        grid = int((int(lens.max()) + 255) // 256) * len(lens) * heads
+        busy = int(np.sum((lens + 255) // 256)) * heads
+        kernels["grid"] = {"workgroups": grid, "empty_frac": round(1.0 - busy / grid, 4)}
 
     # the BF16 comparator: the same attention on the unquantized bf16 Q/K/V, one launch
     # (unsegmented for the chunked workloads), against the FP8 path of this step
@@ -375,9 +458,10 @@ def main(argv=None):
         ds_np = [d.cpu().numpy() for d in descales]
         log("[bench] timing the CPU oracle on a sample ...")
         cb = cpu_baseline(wl, codes_np, ds_np, args.cpu_seconds)
-        log(f"[bench] cpu oracle: {cb['value'] * 1e3:.2f} GFLOP/s on {cb['cores']} threads, "
-            f"{cb['seconds']:.1f} s")
-        result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        log(f"[bench] cpu oracle: {cb['value'] * 1e3:.2f} GFLOP/s on {cb['cores']} BLAS threads "
+            f"({cb['host_cores']} host cores), {cb['seconds']:.1f} s")
+        result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "blas_threads",
+                                                     "host_cores", "kind", "sample")}
     else:
         result["cpu_baseline"] = None
 

@@ -130,6 +130,56 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+# --------------------------------------------------------------------------- argument checks
+#
+# Every tensor argument is checked for dtype, shape and layout first and for its device
+# last, all before the library is called: a host pointer or a mis-shaped operand handed
+# to a kernel would make it read or write outside the caller's buffers.
+
+def _tensor(name: str, t, dtype, shape=None, contiguous: bool = True):
+    """t must be a tensor of `dtype` whose shape matches `shape` (None entries match any
+    size); contiguous unless told otherwise. Returns t."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor, not {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and w != g for w, g in zip(shape, t.shape)):
+            want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
+            raise ValueError(f"{name} must have shape {want}, not {list(t.shape)}")
+    if contiguous and t.numel() > 0 and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _lse_view(name: str, t, heads: int, rows: int):
+    """fp32 [heads, >= rows] with unit column stride; returns its row stride."""
+    import torch
+
+    _tensor(name, t, torch.float32, contiguous=False)
+    if t.dim() != 2 or t.shape[0] != heads or t.shape[1] < rows:
+        raise ValueError(f"{name} must be fp32 [{heads}, >= {rows}], not {list(t.shape)}")
+    if t.numel() > 0 and (t.stride(1) != 1 or (heads > 1 and t.stride(0) < rows)):
+        raise ValueError(f"{name} must have unit column stride and a row stride >= {rows}")
+    return t.stride(0) if heads > 1 else max(rows, t.shape[1])
+
+
+def _on_one_gpu(**named):
+    """Every given tensor (None entries skipped) lives on one CUDA device."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA tensor (it is on {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
 # --------------------------------------------------------------------------- host helpers
 
 def check_descales_host(descale: np.ndarray) -> None:
@@ -153,8 +203,10 @@ def amax_per_head(x, stream=None):
     """x: bf16 [T, H, D] (last dim contiguous). Returns fp32 [H] on x's device."""
     import torch
 
-    if x.dtype != torch.bfloat16 or x.dim() != 3 or (x.numel() > 0 and x.stride(2) != 1):
-        raise ValueError("x must be bf16 [T, H, D] with a contiguous last dim")
+    _tensor("x", x, torch.bfloat16, (None, None, None), contiguous=False)
+    if x.numel() > 0 and x.stride(2) != 1:
+        raise ValueError("x must have a contiguous last dim")
+    _on_one_gpu(x=x)
     amax = torch.empty(x.shape[1], dtype=torch.float32, device=x.device)
     _check(lib().mla_fp8_amax_per_head(_ptr(x), x.stride(0), x.stride(1), x.shape[0], x.shape[1],
                                        x.shape[2], _ptr(amax), _stream(stream)),
@@ -175,22 +227,29 @@ def quant_static(xs: Sequence, descales: Sequence, outs: Optional[Sequence] = No
 def _quant_jobs(xs, descales, outs):
     import torch
 
-    heads = xs[0].shape[1]
+    if outs is not None and len(outs) != len(xs):
+        raise ValueError("need one output per input tensor")
+    heads = None
+    for i, x in enumerate(xs):
+        _tensor(f"x[{i}]", x, torch.bfloat16, (None, heads, None), contiguous=False)
+        heads = x.shape[1]
+        if x.numel() > 0 and x.stride(2) != 1:
+            raise ValueError(f"x[{i}] must have a contiguous last dim")
+        if descales is not None:
+            _tensor(f"descale[{i}]", descales[i], torch.float32, (heads,))
+        if outs is not None:
+            _tensor(f"out[{i}]", outs[i], torch.uint8, tuple(x.shape))
+    named = {f"x[{i}]": x for i, x in enumerate(xs)}
+    if descales is not None:
+        named.update({f"descale[{i}]": d for i, d in enumerate(descales)})
+    if outs is not None:
+        named.update({f"out[{i}]": y for i, y in enumerate(outs)})
+    _on_one_gpu(**named)
     jobs = (QuantJob * len(xs))()
     ys = []
     for i, x in enumerate(xs):
-        if x.dtype != torch.bfloat16 or x.dim() != 3 or x.shape[1] != heads or \
-                (x.numel() > 0 and x.stride(2) != 1):
-            raise ValueError("x must be bf16 [T, H, D] with a contiguous last dim")
-        d = None
-        if descales is not None:
-            d = descales[i]
-            if d.dtype != torch.float32 or d.shape != (heads,) or not d.is_contiguous():
-                raise ValueError("descale must be contiguous fp32 [H]")
+        d = descales[i] if descales is not None else None
         y = outs[i] if outs is not None else torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-        if y.dtype != torch.uint8 or tuple(y.shape) != tuple(x.shape) or \
-                (y.numel() > 0 and not y.is_contiguous()):
-            raise ValueError("output must be contiguous uint8 with x's shape")
         jobs[i] = QuantJob(_ptr(x), x.stride(0), x.stride(1), x.shape[0], x.shape[2],
                            _ptr(d) if d is not None else None, _ptr(y))
         ys.append(y)
@@ -204,12 +263,12 @@ def quant_dynamic(xs: Sequence, outs: Optional[Sequence] = None, descale_out=Non
 
     if not 1 <= len(xs) <= 3:
         raise ValueError("need 1..3 tensors")
+    if descale_out is not None:
+        _tensor("descale_out", descale_out, torch.float32, (len(xs), xs[0].shape[1]))
+        _on_one_gpu(x=xs[0], descale_out=descale_out)
     jobs, ys, heads = _quant_jobs(xs, None, outs)
     if descale_out is None:
         descale_out = torch.empty((len(xs), heads), dtype=torch.float32, device=xs[0].device)
-    if descale_out.dtype != torch.float32 or tuple(descale_out.shape) != (len(xs), heads) or \
-            not descale_out.is_contiguous():
-        raise ValueError("descale_out must be contiguous fp32 [n_tensors, H]")
     _check(lib().mla_fp8_quant_dynamic(jobs, len(xs), heads, _ptr(descale_out), _stream(stream)),
            "mla_fp8_quant_dynamic")
     return ys, descale_out
@@ -222,29 +281,72 @@ def kv_produce(c_kv, k_pe, w_kv_b, descale_k, descale_v, out_bf16: bool = False,
     uint8 codes) and, with out_bf16, also the bf16 K and V."""
     import torch
 
-    for t in (c_kv, k_pe, w_kv_b):
-        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1:
-            raise ValueError("c_kv, k_pe and w_kv_b must be bf16 [rows, cols] with unit column stride")
+    for name, t in (("c_kv", c_kv), ("k_pe", k_pe), ("w_kv_b", w_kv_b)):
+        _tensor(name, t, torch.bfloat16, (None, None), contiguous=False)
+        if t.numel() > 0 and t.stride(1) != 1:
+            raise ValueError(f"{name} must have unit column stride")
     n = c_kv.shape[0]
     if k_pe.shape[0] != n:
         raise ValueError("c_kv and k_pe must have the same number of rows")
     heads = w_kv_b.shape[0] // 256
-    if w_kv_b.shape[0] != heads * 256 or not w_kv_b.is_contiguous():
+    if heads < 1 or w_kv_b.shape[0] != heads * 256 or not w_kv_b.is_contiguous():
         raise ValueError("w_kv_b must be contiguous [n_heads * 256, 512]")
+    _tensor("descale_k", descale_k, torch.float32, (heads,))
+    _tensor("descale_v", descale_v, torch.float32, (heads,))
+    if k8 is not None:
+        _tensor("k8", k8, torch.uint8, (n, heads, D_QK))
+    if v8 is not None:
+        _tensor("v8", v8, torch.uint8, (n, heads, D_V))
+    _on_one_gpu(c_kv=c_kv, k_pe=k_pe, w_kv_b=w_kv_b, descale_k=descale_k, descale_v=descale_v,
+                k8=k8, v8=v8)
     dev = c_kv.device
     if k8 is None:
-        k8 = torch.empty((n, heads, 192), dtype=torch.uint8, device=dev)
+        k8 = torch.empty((n, heads, D_QK), dtype=torch.uint8, device=dev)
     if v8 is None:
         v8 = torch.empty((n, heads, D_V), dtype=torch.uint8, device=dev)
     kb = vb = None
     if out_bf16:
-        kb = torch.empty((n, heads, 192), dtype=torch.bfloat16, device=dev)
+        kb = torch.empty((n, heads, D_QK), dtype=torch.bfloat16, device=dev)
         vb = torch.empty((n, heads, D_V), dtype=torch.bfloat16, device=dev)
     _check(lib().mla_fp8_kv_produce(
         _ptr(c_kv), c_kv.stride(0), _ptr(k_pe), k_pe.stride(0), _ptr(w_kv_b), n, heads,
         w_kv_b.shape[1], k_pe.shape[1], _ptr(descale_k), _ptr(descale_v), _ptr(k8), _ptr(v8),
         _ptr(kb), _ptr(vb), _stream(stream)), "mla_fp8_kv_produce")
     return (k8, v8, kb, vb) if out_bf16 else (k8, v8)
+
+
+def _attention_args(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, lse_stride, descales):
+    """Checks shared by the FP8 and BF16 varlen entry points; returns (out, lse, lse_stride)."""
+    import torch
+
+    _tensor("q", q, dtype, (None, None, D_QK))
+    tq, heads = q.shape[0], q.shape[1]
+    _tensor("k", k, dtype, (None, heads, D_QK))
+    tk = k.shape[0]
+    _tensor("v", v, dtype, (tk, heads, D_V))
+    _tensor("cu_seqlens_q", cu_seqlens_q, torch.int32, (None,))
+    _tensor("cu_seqlens_k", cu_seqlens_k, torch.int32, (cu_seqlens_q.shape[0],))
+    if cu_seqlens_q.shape[0] < 1:
+        raise ValueError("cu_seqlens must hold batch + 1 >= 1 entries")
+    for name, d in descales.items():
+        _tensor(name, d, torch.float32, (heads,))
+    if out is not None:
+        _tensor("out", out, torch.bfloat16, (tq, heads, D_V))
+    if lse is not None:
+        stride = _lse_view("lse", lse, heads, tq)
+        if lse_stride is not None and lse_stride != stride:
+            raise ValueError(f"lse_stride {lse_stride} differs from lse's row stride {stride}")
+        lse_stride = stride
+    _on_one_gpu(q=q, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, out=out,
+                lse=lse, **descales)
+    if out is None:
+        out = torch.empty((tq, heads, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse_stride = tq if lse_stride is None else int(lse_stride)
+        if lse_stride < tq:
+            raise ValueError("lse_stride < total_q")
+        lse = torch.empty((heads, lse_stride), dtype=torch.float32, device=q.device)
+    return out, lse, lse_stride
 
 
 def prefill_varlen(q8, k8, v8, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
@@ -254,21 +356,10 @@ def prefill_varlen(q8, k8, v8, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, ma
     cu_seqlens int32 [B+1] on device. Returns (out bf16 [Tq,H,128], lse fp32 [H, lse_stride])."""
     import torch
 
-    for t in (q8, k8, v8):
-        if t.dtype != torch.uint8 or t.dim() != 3 or not t.is_contiguous():
-            raise ValueError("q8/k8/v8 must be contiguous uint8 [T, H, D]")
-    for t in (cu_seqlens_q, cu_seqlens_k):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise ValueError("cu_seqlens must be contiguous int32")
-    tq, heads = q8.shape[0], q8.shape[1]
-    tk = k8.shape[0]
-    if out is None:
-        out = torch.empty((tq, heads, D_V), dtype=torch.bfloat16, device=q8.device)
-    if lse is None:
-        lse_stride = tq if lse_stride is None else lse_stride
-        lse = torch.empty((heads, lse_stride), dtype=torch.float32, device=q8.device)
-    elif lse_stride is None:
-        lse_stride = lse.stride(0)
+    out, lse, lse_stride = _attention_args(
+        torch.uint8, q8, k8, v8, cu_seqlens_q, cu_seqlens_k, out, lse, lse_stride,
+        {"descale_q": descale_q, "descale_k": descale_k, "descale_v": descale_v})
+    tq, heads, tk = q8.shape[0], q8.shape[1], k8.shape[0]
     batch = cu_seqlens_q.shape[0] - 1
     _check(lib().mla_fp8_prefill_varlen(
         _ptr(q8), _ptr(k8), _ptr(v8), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
@@ -285,21 +376,9 @@ def prefill_varlen_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, 
     (contiguous). Returns (out bf16 [Tq,H,128], lse fp32 [H, lse_stride])."""
     import torch
 
-    for t in (q, k, v):
-        if t.dtype != torch.bfloat16 or t.dim() != 3 or not t.is_contiguous():
-            raise ValueError("q/k/v must be contiguous bf16 [T, H, D]")
-    for t in (cu_seqlens_q, cu_seqlens_k):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise ValueError("cu_seqlens must be contiguous int32")
-    tq, heads = q.shape[0], q.shape[1]
-    tk = k.shape[0]
-    if out is None:
-        out = torch.empty((tq, heads, D_V), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse_stride = tq if lse_stride is None else lse_stride
-        lse = torch.empty((heads, lse_stride), dtype=torch.float32, device=q.device)
-    elif lse_stride is None:
-        lse_stride = lse.stride(0)
+    out, lse, lse_stride = _attention_args(torch.bfloat16, q, k, v, cu_seqlens_q, cu_seqlens_k, out,
+                                           lse, lse_stride, {})
+    tq, heads, tk = q.shape[0], q.shape[1], k.shape[0]
     batch = cu_seqlens_q.shape[0] - 1
     _check(lib().mla_bf16_prefill_varlen(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
@@ -316,21 +395,33 @@ def merge_lse(outs: Sequence, lses: Sequence, out=None, lse_out=None, stream=Non
     n = len(outs)
     if n != len(lses) or n < 1:
         raise ValueError("need one lse per output")
+    _tensor("outs[0]", outs[0], torch.bfloat16, (None, None, D_V))
     tq, heads = outs[0].shape[0], outs[0].shape[1]
-    ld_in = lses[0].stride(0)
-    for o, l_ in zip(outs, lses):
-        if o.dtype != torch.bfloat16 or tuple(o.shape) != (tq, heads, D_V) or not o.is_contiguous():
-            raise ValueError("outs must be contiguous bf16 [T, H, 128]")
-        if l_.dtype != torch.float32 or l_.stride(0) != ld_in or l_.stride(1) != 1:
-            raise ValueError("lses must be fp32 [H, ld] with one common ld")
+    ld_in = None
+    for i, (o, l_) in enumerate(zip(outs, lses)):
+        _tensor(f"outs[{i}]", o, torch.bfloat16, (tq, heads, D_V))
+        ld = _lse_view(f"lses[{i}]", l_, heads, tq)
+        if ld_in is None:
+            ld_in = ld
+        elif ld != ld_in:
+            raise ValueError("lses must share one row stride")
+    if out is not None:
+        _tensor("out", out, torch.bfloat16, (tq, heads, D_V))
+    ld_out = None
+    if lse_out is not None:
+        ld_out = _lse_view("lse_out", lse_out, heads, tq)
+    named = {f"outs[{i}]": o for i, o in enumerate(outs)}
+    named.update({f"lses[{i}]": l_ for i, l_ in enumerate(lses)})
+    _on_one_gpu(out=out, lse_out=lse_out, **named)
     if out is None:
         out = torch.empty_like(outs[0])
     if lse_out is None:
         lse_out = torch.empty((heads, tq), dtype=torch.float32, device=outs[0].device)
+        ld_out = tq
     op = (_c_vp * n)(*[_ptr(o) for o in outs])
     lp = (_c_vp * n)(*[_ptr(l_) for l_ in lses])
     _check(lib().mla_merge_lse(n, op, lp, ld_in, tq, heads, D_V, _ptr(out), _ptr(lse_out),
-                               lse_out.stride(0), _stream(stream)), "mla_merge_lse")
+                               ld_out, _stream(stream)), "mla_merge_lse")
     return out, lse_out
 
 
@@ -347,11 +438,22 @@ def prefill_chunked(q8, k8, v8, descale_q, descale_k, descale_v, softmax_scale: 
     keys with one quantized Q; partials merged in the library. Returns (out, lse)."""
     import torch
 
-    for t in (q8, k8, v8):
-        if t.dtype != torch.uint8 or t.dim() != 3 or not t.is_contiguous():
-            raise ValueError("q8/k8/v8 must be contiguous uint8 [T, H, D]")
+    _tensor("q8", q8, torch.uint8, (None, None, D_QK))
     lq, heads = q8.shape[0], q8.shape[1]
+    _tensor("k8", k8, torch.uint8, (None, heads, D_QK))
     lk = k8.shape[0]
+    _tensor("v8", v8, torch.uint8, (lk, heads, D_V))
+    for name, d in (("descale_q", descale_q), ("descale_k", descale_k), ("descale_v", descale_v)):
+        _tensor(name, d, torch.float32, (heads,))
+    if out is not None:
+        _tensor("out", out, torch.bfloat16, (lq, heads, D_V))
+    lse_stride = lq
+    if lse is not None:
+        lse_stride = _lse_view("lse", lse, heads, lq)
+    if workspace is not None:
+        _tensor("workspace", workspace, torch.uint8, (None,))
+    _on_one_gpu(q8=q8, k8=k8, v8=v8, descale_q=descale_q, descale_k=descale_k,
+                descale_v=descale_v, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty((lq, heads, D_V), dtype=torch.bfloat16, device=q8.device)
     if lse is None:
@@ -359,9 +461,9 @@ def prefill_chunked(q8, k8, v8, descale_q, descale_k, descale_v, softmax_scale: 
     need = chunked_workspace_size(lq, lk, heads, seg_len, causal)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q8.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = 0 if workspace is None else workspace.numel()
     _check(lib().mla_fp8_prefill_chunked(
         _ptr(q8), _ptr(k8), _ptr(v8), lq, lk, heads, _ptr(descale_q), _ptr(descale_k),
         _ptr(descale_v), float(softmax_scale), int(seg_len), int(bool(causal)), _ptr(out), _ptr(lse),
-        lse.stride(0), _ptr(workspace), ws_bytes, _stream(stream)), "mla_fp8_prefill_chunked")
+        lse_stride, _ptr(workspace), ws_bytes, _stream(stream)), "mla_fp8_prefill_chunked")
     return out, lse

@@ -1,6 +1,6 @@
 // Un-absorbed MLA K/V producer fused with the static per-head FP8 quantizer (gfx950).
 //
-// "[ROCm][Kimi-K3] Fold q_b_proj and W_UK for MLA decode" (vLLM #60110), Purpose:
+// vLLM #60110, Purpose:
 // prefill keeps the un-absorbed form, so keys and values are expanded from the latent
 // cache per head; the page gives latent rank 512, 192-wide key heads of which 64 dims
 // are the rope part, and 12 heads per rank. The quantizer is the static per-head one of

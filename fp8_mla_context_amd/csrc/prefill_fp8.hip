@@ -295,8 +295,9 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   constexpr int kPerK = (kKInstr + kWaves - 1) / kWaves;
   constexpr int kPerV = (kVInstr + kWaves - 1) / kWaves;
   // Slot j of a K (V) tile (instruction i = wave + j * kWaves): this lane's tile row and
-  // the byte offset of its chunk within the row. Full tiles use a wave-uniform base plus
-  // row * row_stride + chunk (< 2^31, checked on the host); the ragged last tile clamps rows.
+  // the byte offset of its chunk within the row. Full tiles use a wave-uniform 64-bit tile
+  // base plus row * row_stride + chunk (< 64 * H * 192 < 2^31, checked on the host); the
+  // ragged last tile clamps rows.
   auto dma_row = [&](int j, bool is_k) {
     const int slot = (wave + j * kWaves) * 64 + lane;
     if (is_k) {
@@ -626,8 +627,9 @@ namespace {
 
 // common checks and parameters of both launch forms; returns the number of query tiles
 int prefill_params(const PrefillArgs& a, PrefillParams& prm, int64_t& n_m) {
-  if (a.total_k * static_cast<int64_t>(a.n_heads) * kDqk >= (1ll << 31))
-    return fail(MLA_ERR_UNSUPPORTED, "total_k * n_heads * 192 must be < 2^31");
+  // per-lane DMA offsets within one 64-key tile are 32-bit; tile bases are 64-bit
+  if (static_cast<int64_t>(a.n_heads) * kDqk * kBN >= (1ll << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "n_heads * 192 * 64 must be < 2^31");
   n_m = (static_cast<int64_t>(a.max_seqlen_q) + kBM - 1) / kBM;
   prm = PrefillParams{};
   prm.q = static_cast<const uint8_t*>(a.q);

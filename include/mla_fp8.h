@@ -128,11 +128,11 @@ int mla_fp8_amax_per_head(const void* x, int64_t stride_token, int64_t stride_he
                           float* amax, void* stream);
 
 /*
- * Un-absorbed MLA K/V producer fused with the static quantizer. "[ROCm][Kimi-K3]
- * Fold q_b_proj and W_UK for MLA decode", Purpose: prefill keeps the un-absorbed
- * form, in which keys and values are expanded from the latent cache per head
- * (latent rank 512; the 192-wide key head ends in the 64-dim rope part; 12 heads
- * per rank). The codes follow mla_fp8_quant_static's contract.
+ * Un-absorbed MLA K/V producer fused with the static quantizer. vLLM #60110,
+ * Purpose: prefill keeps the un-absorbed form, in which keys and values are
+ * expanded from the latent cache per head (latent rank 512; the 192-wide key head
+ * ends in the 64-dim rope part; 12 heads per rank). The codes follow
+ * mla_fp8_quant_static's contract.
  *
  *   c_kv          device bf16 latent rows, row t at c_kv + t * c_kv_stride (elements);
  *                 the first 512 elements of a row are used

@@ -28,8 +28,8 @@ What it computes, and the passages it follows (all from the vLLM PR
                the partials merged; must equal the unsegmented result.
   producer.py  the un-absorbed MLA keys and values expanded from the latent cache per
                head (bf16 projection, rope part shared by the heads), then quantized
-               (vLLM PR "[ROCm][Kimi-K3] Fold q_b_proj and W_UK for MLA decode",
-               #60110, Purpose: prefill keeps the un-absorbed form; its shapes).
+               (vLLM #60110, Purpose: prefill keeps the un-absorbed form; its
+               shapes).
 
 Parity pins: every function is checked by tests under ``tests/test_oracle_*.py``
 against closed forms, exhaustive exact-rational rounding, brute force on tiny

@@ -1,7 +1,6 @@
 """Un-absorbed MLA K/V producer followed by the static quantizer.  (Oracle only.)
 
-Follows the vLLM PR "[ROCm][Kimi-K3] Fold q_b_proj and W_UK for MLA decode"
-(#60110), Purpose: decode folds W_UK into the query projection, while prefill
+Follows vLLM #60110, Purpose: decode folds W_UK into the query projection, while prefill
 keeps the un-absorbed form, where keys and values are expanded from the latent
 cache per head. Dimensions from the same page: latent rank 512 (the absorbed
 query ql_nope[.., 12, 512]), a 192-wide query head of which 64 dims are the

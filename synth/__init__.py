@@ -13,6 +13,7 @@ from .inputs import (  # noqa: F401
     Workload,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    make_codes,
     make_latent,
     make_workload,
     random_varlen,

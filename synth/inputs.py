@@ -169,7 +169,8 @@ def _structure(seed: int, lens_spec, use_factors: bool, use_outliers: bool):
 
 
 # name -> (index, description, q lengths, k lengths (None: same as q), causal,
-#          factors, outliers, segment_len)
+#          factors, outliers, segment_len). NC is the non-causal chunk of 4K queries over
+#          65K context keys that the pull request's close comment times.
 CONFIGS = {
     "C1": dict(index=1, desc="1 sequence x 128 tokens, causal, per-head factors",
                lens=[128], k_lens=None, causal=True, factors=True, outliers=False, segment=0),
@@ -186,6 +187,10 @@ CONFIGS = {
                              "8 segments of 16384",
                lens=[131072], k_lens=None, causal=True, factors=True, outliers=True,
                segment=16384),
+    "NC": dict(index=6, desc="4096 queries x 65536 context keys, non-causal (one context "
+                             "chunk); N(0,1)",
+               lens=[4096], k_lens=[65536], causal=False, factors=False, outliers=False,
+               segment=0),
 }
 
 
@@ -257,3 +262,25 @@ def make_latent(seed: int, n_tokens: int, heads: int = N_HEADS):
     cache = f32_to_bf16_bits(rng.standard_normal((n_tokens, LATENT + ROPE), dtype=np.float32))
     w = rng.standard_normal((heads * 256, LATENT), dtype=np.float32) * np.float32(1 / math.sqrt(LATENT))
     return cache, f32_to_bf16_bits(w)
+
+
+def make_codes(seed: int, n_q: int, n_k: int, heads: int = N_HEADS, lo: int = 0x20,
+               hi: int = 0x50):
+    """E4M3 code bytes drawn directly, for contexts too long for a bf16 draw on the host.
+
+    Recipe: ``default_rng(seed).bytes`` gives one random byte per element, Q [n_q, H, 192]
+    first, then K [n_k, H, 192], then V [n_k, H, 128]; bit 7 is the sign and the low 7
+    bits pick a magnitude code on lo..hi (0x20..0x50: values 2^-3 .. 2^3 spread evenly in
+    the exponent) through a fixed 128-entry table. No NaN code can occur. Returns
+    (q8, k8, v8) as uint8 arrays.
+    """
+    rng = np.random.default_rng(seed)
+    table = (lo + (np.arange(128) * (hi - lo + 1)) // 128).astype(np.uint8)
+    table = np.concatenate([table, table | np.uint8(0x80)])
+
+    def draw(shape):
+        n = int(np.prod(shape))
+        raw = np.frombuffer(rng.bytes(n), dtype=np.uint8)
+        return table[raw].reshape(shape)
+
+    return draw((n_q, heads, D_QK)), draw((n_k, heads, D_QK)), draw((n_k, heads, D_V))

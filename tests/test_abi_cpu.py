@@ -201,3 +201,21 @@ def test_quant_dynamic_validation_before_launch(lib):
     assert f((binding.QuantJob * 1)(bad), 1, 12, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
     bad = binding.QuantJob(1 << 12, 192 * 12, 192, 10, 192, None, (1 << 12) + 8)
     assert f((binding.QuantJob * 1)(bad), 1, 12, 1 << 12, None) == binding.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_million_key_context_passes_validation(lib):
+    """A 1,048,576-token context at 12 heads (K codes alone 2.4 GB) is within the
+    library's limits: the prefill's checks accept it, so on a machine without a GPU the
+    call gets as far as the launch (MLA_ERR_HIP), and the chunked plan of 4,096 queries
+    over it in 32,768-key segments has a workspace size. A per-tile offset limit on the
+    head count remains."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("the acceptance probe launches on placeholder pointers; CPU only")
+    lk = 1048576 + 4096
+    assert _prefill(lib, batch=1, max_q=4096, max_k=lk, total_q=4096, total_k=lk) == \
+        binding.MLA_ERR_HIP
+    assert "device" in binding.last_error()
+    assert binding.chunked_workspace_size(4096, lk, 12, 32768, True) > 0
+    assert _prefill(lib, heads=200000) == binding.MLA_ERR_UNSUPPORTED

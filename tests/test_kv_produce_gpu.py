@@ -5,8 +5,11 @@ so the bar is: every bf16 K/V value the kernel produces is the nearest-even bf16
 some value within E = 2^-16 * sum_j |c_j w_j| of the exact sum (in practice all
 but a handful equal the oracle's), and every code is bit-exact for the bf16 value
 the kernel produced (the quantizer decision taken on the same bf16 value on both
-sides). The rope part involves no arithmetic before the quantizer and is
-bit-exact outright. Cases: ragged token counts around the 128-token tile, a row
+sides). End to end, the codes are also compared with the oracle's own producer (its
+exactly rounded bf16 values, then its quantizer): the fraction of codes that differ is
+reported and must stay below 1e-3, and every differing code must be at most one E4M3
+step from the oracle's, at an element whose bf16 value differs. The rope part involves
+no arithmetic before the quantizer and is bit-exact outright. Cases: ragged token counts around the 128-token tile, a row
 stride (latent and rope key sharing one cache row), fewer heads, the optional
 bf16 outputs on or off, and sampled tokens of a 32K-token call.
 """
@@ -17,7 +20,7 @@ import pytest
 import oracle
 from synth import make_latent
 from tests.gpu_helpers import dev, dev_bf16, host
-from tests.parity import bf16_bits_to_f64
+from tests.parity import bf16_bits_to_f64, record
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +71,28 @@ def _check(B, n_tokens, heads, seed, sample=None):
     agree = np.mean(got == exact)
     print(f"T={n_tokens} H={heads}: bf16 values equal to the exact rounding: {agree:.6f}", flush=True)
     assert agree >= 0.999
+    # end to end against the oracle's producer on the same token rows
+    rk8, rv8, _, _ = oracle.kv_produce(cache[rows, :512], cache[rows, 512:], w, dk, dv)
+    codes = np.concatenate([k8[:, :, :128], v8], axis=2)
+    rcodes = np.concatenate([rk8[:, :, :128], rv8], axis=2)
+    assert np.array_equal(k8[:, :, 128:], rk8[:, :, 128:])  # rope part
+    diff = codes != rcodes
+    frac = float(np.mean(diff))
+
+    def ordinal(c):  # E4M3 codes in value order (+0 and -0 both 0)
+        c = c.astype(np.int64)
+        return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+    step = np.abs(ordinal(codes) - ordinal(rcodes))
+    steps_ok = bool(np.all(step[diff] <= 1)) and bool(np.all(got[diff] != exact[diff]))
+    print(f"T={n_tokens} H={heads}: codes differing from the oracle producer: {int(diff.sum())} of "
+          f"{diff.size} ({frac:.2e}), all one step at a differing bf16 value: {steps_ok}", flush=True)
+    record(f"kv_produce T={n_tokens} H={heads}", dict(code_mismatch_frac=frac,
+                                                     code_mismatch=int(diff.sum()),
+                                                     codes=int(diff.size),
+                                                     bf16_exact_frac=float(agree),
+                                                     one_step=steps_ok))
+    assert frac <= 1e-3 and steps_ok
     return k8, v8
 
 
