@@ -344,6 +344,23 @@ def main(argv=None):
             f"{rows} rows: {merge_ms * 1e3:.1f} us ({merge_bytes / merge_ms / 1e6:.0f} GB/s)")
     else:
         kernels["prefill_ms"] = round(prefill_ms, 4)
+        if not wl.causal and wl.batch == 1:
+            # split-KV: the same non-causal chunk through the chunked call, one launch over
+            # 16384-key segments that merges its own partials
+            seg = 16384
+            ws = torch.empty(max(1, B.chunked_workspace_size(wl.total_q, wl.total_k, heads, seg,
+                                                             False)),
+                             dtype=torch.uint8, device="cuda")
+            s_out = torch.empty_like(out)
+            s_lse = torch.empty_like(lse)
+            split_ms, _ = event_ms(torch, lambda: B.prefill_chunked(
+                codes[0], codes[1], codes[2], descales[0], descales[1], descales[2],
+                wl.softmax_scale, seg, False, out=s_out, lse=s_lse, workspace=ws), reps, stream)
+            kernels["split_kv_chunked"] = {"segment": seg, "ms": round(split_ms, 4),
+                                           "TFLOPs": round(flop / (split_ms * 1e-3) / 1e12, 2)}
+            log(f"[bench] split-KV over {seg}-key segments (chunked call, merge in the launch): "
+                f"{split_ms:.3f} ms = {flop / (split_ms * 1e-3) / 1e12:.1f} TFLOP/s")
+            del ws, s_out, s_lse
         # the varlen grid: query tiles of the longest sequence x sequences x heads; the
         # workgroups of shorter sequences past their last row exit at once
         lens = np.diff(wl.cu_seqlens_q)

@@ -15,13 +15,16 @@
 //     diagonal (a causal call with Lq = Lk = r1 - r0); later keys are invisible;
 //   * non-causal requests split every query chunk over all key segments.
 // The host walks the plan: each query chunk's parts run as ONE prefill launch over
-// all its segments (a segment table in the kernel arguments), then one merge, on
-// the caller's stream. Adjacent non-causal segments of a query chunk are attended as
-// one range when the launch keeps at least four workgroups per CU that way (the LSE
-// merge is associative, so this equals merging their partials): fewer fp32 partials are
-// written and merged, and the workspace the plan needs is an upper bound. Partials are kept in fp32 in a caller-provided
-// workspace, so the output is rounded to bf16 once, by the merge; a query
-// chunk with a single part is written straight into `out`.
+// all its segments (a segment table in the kernel arguments) on the caller's stream;
+// the launch merges its own partials: the last workgroup of each (query tile, head) to
+// finish combines the segments' fp32 partials into `out`. Adjacent non-causal segments
+// of a query chunk are attended as one range when the launch keeps at least four
+// workgroups per CU that way (the LSE merge is associative, so this equals merging their
+// partials): fewer fp32 partials are written and merged, and the workspace the plan needs
+// is an upper bound. Partials are kept in fp32 in a caller-provided workspace, so the
+// output is rounded to bf16 once, by the merge; a query chunk with a single part is
+// written straight into `out`. The workspace ends in the merge's arrival counters,
+// zeroed once per call (each launch leaves them zero).
 #include <vector>
 
 #include "mla_internal.h"
@@ -32,7 +35,10 @@ constexpr int kMaxParts = 64;  // the merge kernel's segment limit
 constexpr int64_t kAlign = 256;
 // Launch size below which adjacent non-causal segments stay separate: four workgroups
 // per CU of a 256-CU MI355X, with the prefill's default 256 query rows per workgroup.
-constexpr int64_t kMinBlocks = 4 * 256;
+#ifndef MLA_CHUNK_GROUP_MIN_BLOCKS
+#define MLA_CHUNK_GROUP_MIN_BLOCKS (4 * 256)
+#endif
+constexpr int64_t kMinBlocks = MLA_CHUNK_GROUP_MIN_BLOCKS;
 constexpr int64_t kPrefillRows = 256;
 
 struct Part {
@@ -80,6 +86,12 @@ void group_parts(std::vector<Part>& parts, int64_t blocks_per_part) {
   parts.swap(out);
 }
 
+// arrival counters of the fused merge: one int per (query tile, head) of a query chunk
+int64_t counter_bytes(int64_t rows, int32_t n_heads) {
+  const int64_t bm = mla::prefill_rows_per_block();
+  return align_up((rows + bm - 1) / bm * n_heads * 4);
+}
+
 int64_t max_parts(int64_t lq, int64_t lk, int64_t seg, int32_t causal) {
   if (!causal) return std::max<int64_t>(1, (lk + seg - 1) / seg);
   const int64_t off = lk - lq;
@@ -104,7 +116,8 @@ extern "C" int mla_fp8_chunked_workspace_size(int64_t lq, int64_t lk, int32_t n_
   const int64_t rows = std::min<int64_t>(seg_len, lq);
   const int64_t out_part = align_up(rows * n_heads * 128 * 4);
   const int64_t lse_part = align_up(rows * n_heads * 4);
-  *bytes = (n > 1) ? static_cast<uint64_t>(n * (out_part + lse_part)) : 0u;
+  *bytes = (n > 1) ? static_cast<uint64_t>(n * (out_part + lse_part) + counter_bytes(rows, n_heads))
+                   : 0u;
   return mla::ok();
 }
 
@@ -142,6 +155,8 @@ extern "C" int mla_fp8_prefill_chunked(const void* q, const void* k, const void*
   const int64_t n_max = max_parts(lq, lk, seg, causal);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* lse_ws = ws + n_max * out_part;
+  int32_t* counters = reinterpret_cast<int32_t*>(lse_ws + n_max * lse_part);
+  bool counters_zeroed = false;
   const uint8_t* q8 = static_cast<const uint8_t*>(q);
   const uint8_t* k8 = static_cast<const uint8_t*>(k);
   const uint8_t* v8 = static_cast<const uint8_t*>(v);
@@ -151,8 +166,6 @@ extern "C" int mla_fp8_prefill_chunked(const void* q, const void* k, const void*
   const int64_t orow = static_cast<int64_t>(n_heads) * 128 * 2;
 
   std::vector<Part> parts;
-  const void* outs[kMaxParts];
-  const float* lses[kMaxParts];
   for (int64_t r0 = 0; r0 < lq; r0 += seg) {
     const int64_t r1 = std::min(lq, r0 + seg);
     const int64_t rows = r1 - r0;
@@ -172,23 +185,24 @@ extern "C" int mla_fp8_prefill_chunked(const void* q, const void* k, const void*
       continue;
     }
     // all parts of this query chunk in ONE launch (fp32 partials in the workspace),
-    // non-causal segments first (the plan lists the causal diagonal last), then the merge
+    // non-causal segments first (the plan lists the causal diagonal last), merged by the
+    // launch itself into the chunk's output rows
+    if (!counters_zeroed) {
+      st = mla::zero_ints(counters, counter_bytes(rows_max, n_heads) / 4, s);
+      if (st != MLA_OK) return st;
+      counters_zeroed = true;
+    }
     mla::PrefillSegment segs[kMaxParts];
     for (int i = 0; i < n; ++i) {
       const Part& pt = parts[i];
       segs[i] = mla::PrefillSegment{pt.k0, static_cast<int32_t>(pt.k1 - pt.k0), pt.causal,
                                     ws + i * out_part,
                                     reinterpret_cast<float*>(lse_ws + i * lse_part)};
-      outs[i] = segs[i].out;
-      lses[i] = segs[i].lse;
     }
     mla::PrefillArgs a{q8 + r0 * qrow, k8, v8, nullptr, nullptr, 1, static_cast<int32_t>(rows),
                        rows, lk, n_heads, descale_q, descale_k, descale_v, softmax_scale, 0,
-                       nullptr, 1, nullptr, rows};
+                       out8 + r0 * orow, 1, lse ? lse + r0 : nullptr, lse_stride, rows, counters};
     st = mla::prefill_launch_segments(a, segs, n, s);
-    if (st != MLA_OK) return st;
-    st = mla::merge_launch(n, outs, 1, lses, rows, rows, n_heads, out8 + r0 * orow,
-                           lse ? lse + r0 : nullptr, lse_stride, s);
     if (st != MLA_OK) return st;
   }
   return mla::ok();

@@ -70,6 +70,12 @@ struct PrefillArgs {
   int32_t out_f32;
   float* lse;
   int64_t lse_stride;
+  // multi-segment launches only: the partials' LSE row stride, and the arrival counters
+  // of the fused merge (NULL: no merge; else ceil(max_seqlen_q / 256) * n_heads zeroed
+  // ints, left zeroed); with the merge, out / lse / lse_stride above receive the merged
+  // bf16 result
+  int64_t seg_lse_stride = 0;
+  int32_t* counters = nullptr;
 };
 
 // One context segment of a multi-segment launch: the same query rows attend keys
@@ -85,9 +91,14 @@ struct PrefillSegment {
 };
 int prefill_launch(const PrefillArgs& a, hipStream_t stream);
 // one launch over n segments for the query rows of a (a.batch == 1, no cu_seqlens; a.k/a.v
-// hold all keys, a.total_k of them; a.out, a.lse and a.causal are ignored)
+// hold all keys, a.total_k of them; a.causal is ignored; a.out and a.lse are the merged
+// result when a.counters is set, else ignored)
 int prefill_launch_segments(const PrefillArgs& a, const PrefillSegment* segs, int n,
                             hipStream_t stream);
+// query rows per workgroup of the FP8 prefill (the tile of the merge counters)
+int prefill_rows_per_block();
+// zero n ints on the stream (a fill kernel, so that the call can be graph-captured)
+int zero_ints(int32_t* p, int64_t n, hipStream_t stream);
 
 // LSE merge launch with validated arguments; partials are bf16 or (in_f32) fp32.
 int merge_launch(int32_t n_segments, const void* const* outs, int32_t in_f32,

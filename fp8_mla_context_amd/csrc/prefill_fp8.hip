@@ -48,6 +48,8 @@
 //    diagonal or the ragged end are masked element-wise.
 //  * Epilogue: out = O * dv / l in bf16 (fp32 for the partials of a chunked pass),
 //    lse = ln2 * (m + log2 l).
+#include <algorithm>
+
 #include "mla_internal.h"
 #include "device_common.h"
 
@@ -108,6 +110,12 @@ struct PrefillParams {
   int32_t out_f32;  // 1: out is fp32 (partials of a chunked pass), 0: bf16
   int32_t xcd_order;  // 1: XCD-aware block order (one sequence, H % 4 == 0, even tile count)
   float scale_log2;
+  // multi-segment launches: row stride of the segments' partial LSEs, and (if not null)
+  // one arrival counter per (query tile, head), all zero at launch: the last workgroup of
+  // a tile to finish merges the segments' fp32 partials into out (bf16) and lse
+  // (lse_stride) and sets the counter back to zero
+  int64_t seg_lse_stride;
+  int32_t* counters;
 };
 
 // Context segments of a multi-segment launch (see mla::PrefillSegment); N = 1 for the
@@ -145,6 +153,19 @@ __device__ __forceinline__ v2i read_tr8(const uint8_t* lds_ptr) {
       (__attribute__((address_space(3))) v2i*)(lds_ptr));
 }
 
+// Partials of a launch that merges its own segments are exchanged between workgroups on
+// different XCDs, whose L2 caches are not coherent with each other. They are written and
+// read with agent-coherent accesses (the sc1 form the compiler gives agent-scope atomic
+// loads and stores), so neither side needs a whole-L2 write-back or invalidate.
+__device__ __forceinline__ void store16_agent(float* ptr, float4 v) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const v4f d = {v.x, v.y, v.z, v.w};
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(ptr), "v"(d) : "memory");
+}
+__device__ __forceinline__ float load_agent(const float* ptr) {
+  return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // S^T block for one tile: two 32-key blocks, K-dim 192 = 3 x 64
 __device__ __forceinline__ void qk_tile(const uint8_t* kl, int col, int g, const v8i qf[3],
                                         v16f s[2]) {
@@ -165,6 +186,61 @@ __device__ __forceinline__ void qk_tile(const uint8_t* kl, int col, int g, const
 // 32-dim block per 16 lanes) this spreads every group of 16 or 32 lanes over distinct
 // banks, with 32 or with 64 four-byte banks.
 __device__ __forceinline__ int v_swizzle(int key) { return (key & 3) | (((key >> 3) & 1) << 2); }
+
+// Fused LSE merge of a multi-segment launch. Every workgroup of query tile m_tile and
+// head h has written its segment's fp32 partial out and LSE (agent-coherent stores, all
+// completed before the workgroup's barrier); the last of the st.n workgroups of that
+// tile to count its arrival combines them for the tile's rows [row0, row0 + rows):
+//   L = ln sum_s exp(L_s),  out = sum_s exp(L_s - L) * out_s   (all L_s = -inf: 0, -inf)
+// with the arithmetic of the separate merge kernel (same order over s), reading the
+// partials with agent-coherent loads issued after the counter returned.
+template <int kNSeg>
+__device__ __forceinline__ void merge_on_last_arrival(const PrefillParams& p,
+                                                      const SegTable<kNSeg>& st, int h, int m_tile,
+                                                      int row0, int rows) {
+  __shared__ int last;
+  const int tid = threadIdx.x;
+  int32_t* counter = p.counters + static_cast<int64_t>(m_tile) * p.n_heads + h;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are done
+  __syncthreads();                                  // ... and every other wave's
+  if (tid == 0)
+    last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            st.n - 1) ? 1 : 0;
+  __syncthreads();
+  if (!last) return;
+  if (tid == 0)  // ready for the next launch on this stream
+    __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int H = p.n_heads;
+  for (int item = tid; item < rows * 16; item += kThreads) {
+    const int64_t row = row0 + (item >> 4);
+    const int c8 = item & 15;
+    const int64_t li = static_cast<int64_t>(h) * p.seg_lse_stride + row;
+    float m = -INFINITY;
+    for (int s = 0; s < st.n; ++s) m = fmaxf(m, load_agent(st.e[s].lse + li));
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float tot = 0.f;
+    const int64_t eo = (row * H + h) * kDv + 8 * c8;
+    if (m != -INFINITY) {
+      for (int s = 0; s < st.n; ++s) {
+        const float w = __expf(load_agent(st.e[s].lse + li) - m);  // 0 for an empty segment
+        tot += w;
+        const float* src = static_cast<const float*>(st.e[s].out) + eo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += w * load_agent(src + i);
+      }
+    }
+    const float inv = (m != -INFINITY) ? 1.0f / tot : 0.0f;
+    uint4 o;
+    o.x = mla::f32_to_bf16_rne(acc[0] * inv) | (mla::f32_to_bf16_rne(acc[1] * inv) << 16);
+    o.y = mla::f32_to_bf16_rne(acc[2] * inv) | (mla::f32_to_bf16_rne(acc[3] * inv) << 16);
+    o.z = mla::f32_to_bf16_rne(acc[4] * inv) | (mla::f32_to_bf16_rne(acc[5] * inv) << 16);
+    o.w = mla::f32_to_bf16_rne(acc[6] * inv) | (mla::f32_to_bf16_rne(acc[7] * inv) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + eo) = o;
+    if (c8 == 0 && p.lse != nullptr)
+      p.lse[static_cast<int64_t>(h) * p.lse_stride + row] =
+          (m != -INFINITY) ? m + __logf(tot) : -INFINITY;
+  }
+}
 
 template <int kNSeg>
 __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(PrefillParams p,
@@ -592,13 +668,19 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     const int64_t obase = (q0 + my_row) * (static_cast<int64_t>(H) * kDv) + h * kDv;
     if (p.out_f32) {
       float* op = static_cast<float*>(out_ptr) + obase;
+      const bool coherent = kNSeg > 1 && p.counters != nullptr;  // read by another workgroup
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int grp4 = 0; grp4 < 4; ++grp4)
-          *reinterpret_cast<float4*>(op + 32 * db + 8 * grp4 + 4 * g) =
-              make_float4(o[db][4 * grp4 + 0] * inv, o[db][4 * grp4 + 1] * inv,
-                          o[db][4 * grp4 + 2] * inv, o[db][4 * grp4 + 3] * inv);
+        for (int grp4 = 0; grp4 < 4; ++grp4) {
+          const float4 v = make_float4(o[db][4 * grp4 + 0] * inv, o[db][4 * grp4 + 1] * inv,
+                                       o[db][4 * grp4 + 2] * inv, o[db][4 * grp4 + 3] * inv);
+          float* dst = op + 32 * db + 8 * grp4 + 4 * g;
+          if (coherent)
+            store16_agent(dst, v);
+          else
+            *reinterpret_cast<float4*>(dst) = v;
+        }
     } else {
       uint16_t* op = static_cast<uint16_t*>(out_ptr) + obase;
 #pragma unroll
@@ -613,9 +695,18 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
               make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
         }
     }
-    if (g == 0 && lse_ptr != nullptr)
-      lse_ptr[static_cast<int64_t>(h) * p.lse_stride + q0 + my_row] =
-          (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (g == 0 && lse_ptr != nullptr) {
+      float* lp = lse_ptr + static_cast<int64_t>(h) * (kNSeg > 1 ? p.seg_lse_stride : p.lse_stride) +
+                  q0 + my_row;
+      const float lv = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      if (kNSeg > 1 && p.counters != nullptr)
+        __hip_atomic_store(lp, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        *lp = lv;
+    }
+  }
+  if constexpr (kNSeg > 1) {
+    if (p.counters != nullptr) merge_on_last_arrival(p, st, h, m_tile, row0, min(kBM, Lq - row0));
   }
 }
 
@@ -651,10 +742,28 @@ int prefill_params(const PrefillArgs& a, PrefillParams& prm, int64_t& n_m) {
   prm.n_m_tiles = static_cast<int32_t>(n_m);
   prm.causal = a.causal;
   prm.scale_log2 = a.softmax_scale * 1.44269504088896340736f;
+  prm.seg_lse_stride = a.seg_lse_stride;
+  prm.counters = a.counters;
   return MLA_OK;
 }
 
+__global__ void zero_ints_kernel(int32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+
 }  // namespace
+
+int prefill_rows_per_block() { return kBM; }
+
+int zero_ints(int32_t* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return ok();
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p,
+                     n);
+  return check_launch("zero_ints_kernel");
+}
 
 int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   if (a.total_q == 0 || a.batch == 0 || a.max_seqlen_q == 0) return ok();
@@ -677,6 +786,10 @@ int prefill_launch_segments(const PrefillArgs& a, const PrefillSegment* segs, in
     return fail(MLA_ERR_INVALID_ARGUMENT, "%d segments not in 1..%d", n, kMaxPrefillSegments);
   if (a.batch != 1 || a.cu_q != nullptr)
     return fail(MLA_ERR_INVALID_ARGUMENT, "segments need one sequence without cu_seqlens");
+  if (a.counters != nullptr &&
+      (a.out_f32 != 1 || a.out == nullptr || !aligned16(a.out) || a.seg_lse_stride < a.total_q ||
+       (a.lse != nullptr && a.lse_stride < a.total_q)))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "fused merge needs fp32 partials and a bf16 output");
   if (a.total_q == 0 || a.max_seqlen_q == 0) return ok();
   PrefillParams prm;
   int64_t n_m = 0;

@@ -253,25 +253,31 @@ int mla_merge_lse(int32_t n_segments, const void* const* outs, const float* cons
 /*
  * Attention of Lq queries that are the last Lq of Lk tokens (bottom-right
  * causal alignment; causal = 0: every key visible), computed over context
- * segments of seg_len keys with ONE quantized Q, partials merged by
- * mla_merge_lse. Follows "[ROCm][MLA] Add guarded gfx942 FP8 context prefill",
- * "What this PR does" (Q quantized once per context pass, its per-head scale
- * reused across context segments). The segmentation (not given on the pages):
- * queries in chunks of seg_len rows; cached keys [0, Lk - Lq) in segments of
- * seg_len, seen in full by every query; for query chunk [r0, r1) the own keys
- * [Lk-Lq, Lk-Lq+r0) in segments of seg_len seen in full, then the diagonal
- * [Lk-Lq+r0, Lk-Lq+r1) as a causal call. Adjacent non-causal segments of a query
- * chunk are attended as one range when the launch keeps at least four workgroups
- * per CU that way (the merge is associative). Partials stay in fp32 (workspace)
- * and the merged output is rounded to bf16 once. The result equals
- * mla_fp8_prefill_varlen on the whole sequence up to rounding.
+ * segments of seg_len keys with ONE quantized Q, partials merged by the
+ * log-sum-exp rule of mla_merge_lse. Follows "[ROCm][MLA] Add guarded gfx942 FP8
+ * context prefill", "What this PR does" (Q quantized once per context pass, its
+ * per-head scale reused across context segments). The segmentation (not given on
+ * the pages): queries in chunks of seg_len rows; cached keys [0, Lk - Lq) in
+ * segments of seg_len, seen in full by every query; for query chunk [r0, r1) the
+ * own keys [Lk-Lq, Lk-Lq+r0) in segments of seg_len seen in full, then the diagonal
+ * [Lk-Lq+r0, Lk-Lq+r1) as a causal call. Each query chunk is ONE kernel launch over
+ * all its segments, which also merges them: the last workgroup of every (256-row
+ * query tile, head) to finish combines the segments' partials. Adjacent non-causal
+ * segments of a query chunk are attended as one range when the launch keeps at least
+ * four workgroups per CU that way (the merge is associative). Partials stay in fp32
+ * (workspace) and the merged output is rounded to bf16 once. The result equals
+ * mla_fp8_prefill_varlen on the whole sequence up to rounding. With causal = 0 and
+ * seg_len >= Lq this is split-KV attention: one launch that spreads every (query
+ * tile, head) over the key segments.
  *
  *   q, k, v     device E4M3, contiguous [Lq, H, 192], [Lk, H, 192], [Lk, H, 128]
  *   out, lse    as mla_fp8_prefill_varlen (lse may be NULL; lse_stride >= Lq)
  *   workspace   device scratch of mla_fp8_chunked_workspace_size() bytes, 16-byte
- *               aligned (may be NULL when that size is 0); contents are overwritten
+ *               aligned (may be NULL when that size is 0); contents are overwritten;
+ *               calls that share a workspace must not overlap in time
  *   causal = 1 requires Lk >= Lq. At most 64 segments per query chunk
- *   (MLA_ERR_UNSUPPORTED beyond). Enqueues several launches on `stream`.
+ *   (MLA_ERR_UNSUPPORTED beyond). Enqueues one launch per query chunk on `stream`,
+ *   after one small launch that clears the merge counters in the workspace.
  */
 int mla_fp8_prefill_chunked(const void* q, const void* k, const void* v, int64_t lq, int64_t lk,
                             int32_t n_heads, const float* descale_q, const float* descale_k,
