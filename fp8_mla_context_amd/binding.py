@@ -78,6 +78,9 @@ SIGNATURES = {
         _c_i32, _c_vp, _c_vp, _c_i64, _c_vp, ctypes.c_uint64, _c_vp]),
     "mla_fp8_chunked_workspace_size": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                                       ctypes.POINTER(ctypes.c_uint64)]),
+    "mla_fp8_prefill_chunked_noalloc": (ctypes.c_int, [
+        _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_i32,
+        _c_i32, _c_vp, _c_vp, _c_i64, _c_vp]),
     "mla_check_descales_host": (ctypes.c_int, [_c_fp, _c_i32]),
     "mla_descale_from_amax_host": (ctypes.c_int, [_c_fp, _c_i32, _c_fp]),
 }
@@ -430,6 +433,37 @@ def chunked_workspace_size(lq: int, lk: int, n_heads: int, seg_len: int, causal:
     _check(lib().mla_fp8_chunked_workspace_size(lq, lk, n_heads, seg_len, int(bool(causal)),
                                                 ctypes.byref(n)), "mla_fp8_chunked_workspace_size")
     return int(n.value)
+
+
+def prefill_chunked_noalloc(q8, k8, v8, descale_q, descale_k, descale_v, softmax_scale: float,
+                            seg_len: int, causal: bool = True, out=None, lse=None, stream=None):
+    """prefill_chunked with the library's own device scratch instead of a workspace: the call
+    itself allocates nothing (pass out and lse to keep this wrapper from allocating them)."""
+    import torch
+
+    _tensor("q8", q8, torch.uint8, (None, None, D_QK))
+    lq, heads = q8.shape[0], q8.shape[1]
+    _tensor("k8", k8, torch.uint8, (None, heads, D_QK))
+    lk = k8.shape[0]
+    _tensor("v8", v8, torch.uint8, (lk, heads, D_V))
+    for name, d in (("descale_q", descale_q), ("descale_k", descale_k), ("descale_v", descale_v)):
+        _tensor(name, d, torch.float32, (heads,))
+    if out is not None:
+        _tensor("out", out, torch.bfloat16, (lq, heads, D_V))
+    lse_stride = lq
+    if lse is not None:
+        lse_stride = _lse_view("lse", lse, heads, lq)
+    _on_one_gpu(q8=q8, k8=k8, v8=v8, descale_q=descale_q, descale_k=descale_k,
+                descale_v=descale_v, out=out, lse=lse)
+    if out is None:
+        out = torch.empty((lq, heads, D_V), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((heads, lq), dtype=torch.float32, device=q8.device)
+    _check(lib().mla_fp8_prefill_chunked_noalloc(
+        _ptr(q8), _ptr(k8), _ptr(v8), lq, lk, heads, _ptr(descale_q), _ptr(descale_k),
+        _ptr(descale_v), float(softmax_scale), int(seg_len), int(bool(causal)), _ptr(out), _ptr(lse),
+        lse_stride, _stream(stream)), "mla_fp8_prefill_chunked_noalloc")
+    return out, lse
 
 
 def prefill_chunked(q8, k8, v8, descale_q, descale_k, descale_v, softmax_scale: float, seg_len: int,

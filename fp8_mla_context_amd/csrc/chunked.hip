@@ -25,9 +25,15 @@
 // output is rounded to bf16 once, by the merge; a query chunk with a single part is
 // written straight into `out`. The workspace ends in the merge's arrival counters,
 // zeroed once per call (each launch leaves them zero).
+#include <mutex>
 #include <vector>
 
 #include "mla_internal.h"
+
+// Device scratch of mla_fp8_prefill_chunked_noalloc (partials, LSEs and merge counters of
+// its launches); each GPU the library runs on holds one copy until the process ends.
+static constexpr int64_t kScratchBytes = MLA_FP8_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -100,24 +106,152 @@ int64_t max_parts(int64_t lq, int64_t lk, int64_t seg, int32_t causal) {
   return (off + seg - 1) / seg + (last_r0 + seg - 1) / seg + 1;
 }
 
+// Workspace layout for launches of up to `rows` query rows and n parts: n fp32 partial
+// outputs, n partial LSEs, then the merge counters.
+int64_t layout_bytes(int64_t n, int64_t rows, int32_t n_heads) {
+  if (n <= 1) return 0;
+  return n * (align_up(rows * n_heads * 128 * 4) + align_up(rows * n_heads * 4)) +
+         counter_bytes(rows, n_heads);
+}
+
+// Checks shared by the entry points; n_max = the plan's most parts per query chunk.
+int check_plan(int64_t lq, int64_t lk, int32_t n_heads, int32_t seg_len, int32_t causal,
+               int64_t* n_max) {
+  if (lq < 0 || lk < 0 || n_heads < 1 || seg_len < 1 || (causal != 0 && causal != 1))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "bad size, head count, segment length or causal");
+  if (causal && lk < lq)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "causal chunked prefill needs Lk >= Lq");
+  *n_max = max_parts(lq, lk, seg_len, causal);
+  if (*n_max > kMaxParts)
+    return mla::fail(MLA_ERR_UNSUPPORTED, "%lld parts per query chunk exceed %d",
+                     static_cast<long long>(*n_max), kMaxParts);
+  return MLA_OK;
+}
+
+int check_call(const void* q, const void* k, const void* v, int64_t lq, int64_t lk,
+               int32_t n_heads, const float* descale_q, const float* descale_k,
+               const float* descale_v, float softmax_scale, int32_t seg_len, int32_t causal,
+               void* out, float* lse, int64_t lse_stride, int64_t* n_max) {
+  int st = mla::prefill_check_common(n_heads, 192, 128, softmax_scale, causal);
+  if (st != MLA_OK) return st;
+  st = check_plan(lq, lk, n_heads, seg_len, causal, n_max);
+  if (st != MLA_OK) return st;
+  if (lq >= (1ll << 31) || lk >= (1ll << 31))
+    return mla::fail(MLA_ERR_UNSUPPORTED, "Lq and Lk must be < 2^31");
+  if (lq == 0) return MLA_OK;
+  if (q == nullptr || out == nullptr || descale_q == nullptr || descale_k == nullptr ||
+      descale_v == nullptr || (lk > 0 && (k == nullptr || v == nullptr)))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!mla::aligned16(q) || !mla::aligned16(k) || !mla::aligned16(v) || !mla::aligned16(out))
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
+  if (lse != nullptr && lse_stride < lq)
+    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "lse_stride < Lq");
+  return MLA_OK;
+}
+
+// Walk the plan with launches of at most rows_per_launch query rows (the whole query chunk,
+// or a multiple of the prefill's row tile): the rows [a, b) of query chunk [r0, r1) attend
+// the chunk's parts, with the causal diagonal cut to keys [off + r0, off + b) (bottom-right
+// alignment keeps every row's visible keys). ws holds layout_bytes(n_max, rows_per_launch).
+int run_plan(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, int64_t lq, int64_t lk,
+             int32_t n_heads, const float* descale_q, const float* descale_k,
+             const float* descale_v, float softmax_scale, int64_t seg, int32_t causal,
+             uint8_t* out8, float* lse, int64_t lse_stride, uint8_t* ws, int64_t n_max,
+             int64_t rows_per_launch, hipStream_t s) {
+  const int64_t out_part = align_up(rows_per_launch * n_heads * 128 * 4);
+  const int64_t lse_part = align_up(rows_per_launch * n_heads * 4);
+  uint8_t* lse_ws = ws + n_max * out_part;
+  int32_t* counters = reinterpret_cast<int32_t*>(lse_ws + n_max * lse_part);
+  bool counters_zeroed = false;
+  const int64_t qrow = static_cast<int64_t>(n_heads) * 192;
+  const int64_t vrow = static_cast<int64_t>(n_heads) * 128;
+  const int64_t orow = static_cast<int64_t>(n_heads) * 128 * 2;
+  const int64_t off = lk - lq;
+  std::vector<Part> chunk, parts;
+  int st = MLA_OK;
+  for (int64_t r0 = 0; r0 < lq; r0 += seg) {
+    const int64_t r1 = std::min(lq, r0 + seg);
+    if (!chunk_parts(lq, lk, seg, causal, r0, r1, chunk))
+      return mla::fail(MLA_ERR_INVALID_ARGUMENT, "no chunk plan");
+    for (int64_t a = r0; a < r1; a += rows_per_launch) {
+      const int64_t b = std::min(r1, a + rows_per_launch);
+      const int64_t rows = b - a;
+      parts = chunk;
+      if (causal) parts.back().k1 = off + b;  // the diagonal is the plan's last part
+      group_parts(parts, (rows + kPrefillRows - 1) / kPrefillRows * n_heads);
+      const int n = static_cast<int>(parts.size());
+      if (n == 1) {
+        // a single part is written straight into the output rows
+        const Part& pt = parts[0];
+        mla::PrefillArgs pa{q8 + a * qrow, k8 + pt.k0 * qrow, v8 + pt.k0 * vrow, nullptr, nullptr,
+                            1, static_cast<int32_t>(rows), rows, pt.k1 - pt.k0, n_heads, descale_q,
+                            descale_k, descale_v, softmax_scale, pt.causal, out8 + a * orow, 0,
+                            lse ? lse + a : nullptr, lse_stride};
+        st = mla::prefill_launch(pa, s);
+        if (st != MLA_OK) return st;
+        continue;
+      }
+      // all parts of these rows in ONE launch (fp32 partials in the workspace), non-causal
+      // segments first (the plan lists the causal diagonal last), merged by the launch
+      // itself into the output rows
+      if (!counters_zeroed) {
+        st = mla::zero_ints(counters, counter_bytes(rows_per_launch, n_heads) / 4, s);
+        if (st != MLA_OK) return st;
+        counters_zeroed = true;
+      }
+      mla::PrefillSegment segs[kMaxParts];
+      for (int i = 0; i < n; ++i) {
+        const Part& pt = parts[i];
+        segs[i] = mla::PrefillSegment{pt.k0, static_cast<int32_t>(pt.k1 - pt.k0), pt.causal,
+                                      ws + i * out_part,
+                                      reinterpret_cast<float*>(lse_ws + i * lse_part)};
+      }
+      mla::PrefillArgs pa{q8 + a * qrow, k8, v8, nullptr, nullptr, 1, static_cast<int32_t>(rows),
+                          rows, lk, n_heads, descale_q, descale_k, descale_v, softmax_scale, 0,
+                          out8 + a * orow, 1, lse ? lse + a : nullptr, lse_stride, rows,
+                          counters};
+      st = mla::prefill_launch_segments(pa, segs, n, s);
+      if (st != MLA_OK) return st;
+    }
+  }
+  return mla::ok();
+}
+
+// Scratch of the entry point that allocates nothing: one copy per GPU, resolved with
+// hipGetSymbolAddress on the first call on each device (in host code `scratch` names a
+// host-side stand-in, never the device memory itself).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(uint8_t** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return mla::fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return mla::fail(MLA_ERR_UNSUPPORTED, "device %d beyond the %d this library tracks", dev,
+                     kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return mla::fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" int mla_fp8_chunked_workspace_size(int64_t lq, int64_t lk, int32_t n_heads,
                                               int32_t seg_len, int32_t causal, uint64_t* bytes) {
   if (bytes == nullptr) return mla::fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
-  if (lq < 0 || lk < 0 || n_heads < 1 || seg_len < 1 || (causal != 0 && causal != 1))
-    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "bad size, head count, segment length or causal");
-  if (causal && lk < lq)
-    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "causal chunked prefill needs Lk >= Lq");
-  const int64_t n = max_parts(lq, lk, seg_len, causal);
-  if (n > kMaxParts)
-    return mla::fail(MLA_ERR_UNSUPPORTED, "%lld parts per query chunk exceed %d",
-                     static_cast<long long>(n), kMaxParts);
-  const int64_t rows = std::min<int64_t>(seg_len, lq);
-  const int64_t out_part = align_up(rows * n_heads * 128 * 4);
-  const int64_t lse_part = align_up(rows * n_heads * 4);
-  *bytes = (n > 1) ? static_cast<uint64_t>(n * (out_part + lse_part) + counter_bytes(rows, n_heads))
-                   : 0u;
+  int64_t n = 0;
+  const int st = check_plan(lq, lk, n_heads, seg_len, causal, &n);
+  if (st != MLA_OK) return st;
+  *bytes = static_cast<uint64_t>(layout_bytes(n, std::min<int64_t>(seg_len, lq), n_heads));
   return mla::ok();
 }
 
@@ -127,83 +261,56 @@ extern "C" int mla_fp8_prefill_chunked(const void* q, const void* k, const void*
                                        float softmax_scale, int32_t seg_len, int32_t causal,
                                        void* out, float* lse, int64_t lse_stride, void* workspace,
                                        uint64_t workspace_bytes, void* stream) {
-  int st = mla::prefill_check_common(n_heads, 192, 128, softmax_scale, causal);
-  if (st != MLA_OK) return st;
-  uint64_t need = 0;
-  st = mla_fp8_chunked_workspace_size(lq, lk, n_heads, seg_len, causal, &need);
-  if (st != MLA_OK) return st;
-  if (lq >= (1ll << 31) || lk >= (1ll << 31))
-    return mla::fail(MLA_ERR_UNSUPPORTED, "Lq and Lk must be < 2^31");
-  if (lq == 0) return mla::ok();
-  if (q == nullptr || out == nullptr || descale_q == nullptr || descale_k == nullptr ||
-      descale_v == nullptr || (lk > 0 && (k == nullptr || v == nullptr)))
-    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer");
-  if (!mla::aligned16(q) || !mla::aligned16(k) || !mla::aligned16(v) || !mla::aligned16(out))
-    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
-  if (lse != nullptr && lse_stride < lq)
-    return mla::fail(MLA_ERR_INVALID_ARGUMENT, "lse_stride < Lq");
+  int64_t n_max = 0;
+  int st = check_call(q, k, v, lq, lk, n_heads, descale_q, descale_k, descale_v, softmax_scale,
+                      seg_len, causal, out, lse, lse_stride, &n_max);
+  if (st != MLA_OK || lq == 0) return st == MLA_OK ? mla::ok() : st;
+  const int64_t rows = std::min<int64_t>(seg_len, lq);
+  const uint64_t need = static_cast<uint64_t>(layout_bytes(n_max, rows, n_heads));
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !mla::aligned16(workspace)))
     return mla::fail(MLA_ERR_INVALID_ARGUMENT,
                      "workspace must be 16-byte aligned and hold %llu bytes",
                      static_cast<unsigned long long>(need));
+  return run_plan(static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
+                  static_cast<const uint8_t*>(v), lq, lk, n_heads, descale_q, descale_k, descale_v,
+                  softmax_scale, seg_len, causal, static_cast<uint8_t*>(out), lse, lse_stride,
+                  static_cast<uint8_t*>(workspace), n_max, rows, static_cast<hipStream_t>(stream));
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t seg = seg_len;
-  const int64_t rows_max = std::min<int64_t>(seg, lq);
-  const int64_t out_part = align_up(rows_max * n_heads * 128 * 4);
-  const int64_t lse_part = align_up(rows_max * n_heads * 4);
-  const int64_t n_max = max_parts(lq, lk, seg, causal);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint8_t* lse_ws = ws + n_max * out_part;
-  int32_t* counters = reinterpret_cast<int32_t*>(lse_ws + n_max * lse_part);
-  bool counters_zeroed = false;
-  const uint8_t* q8 = static_cast<const uint8_t*>(q);
-  const uint8_t* k8 = static_cast<const uint8_t*>(k);
-  const uint8_t* v8 = static_cast<const uint8_t*>(v);
-  uint8_t* out8 = static_cast<uint8_t*>(out);
-  const int64_t qrow = static_cast<int64_t>(n_heads) * 192;
-  const int64_t vrow = static_cast<int64_t>(n_heads) * 128;
-  const int64_t orow = static_cast<int64_t>(n_heads) * 128 * 2;
-
-  std::vector<Part> parts;
-  for (int64_t r0 = 0; r0 < lq; r0 += seg) {
-    const int64_t r1 = std::min(lq, r0 + seg);
-    const int64_t rows = r1 - r0;
-    if (!chunk_parts(lq, lk, seg, causal, r0, r1, parts))
-      return mla::fail(MLA_ERR_INVALID_ARGUMENT, "no chunk plan");
-    group_parts(parts, (rows + kPrefillRows - 1) / kPrefillRows * n_heads);
-    const int n = static_cast<int>(parts.size());
-    if (n == 1) {
-      // a single part is written straight into the output rows
-      const Part& pt = parts[0];
-      mla::PrefillArgs a{q8 + r0 * qrow, k8 + pt.k0 * qrow, v8 + pt.k0 * vrow, nullptr, nullptr,
-                         1, static_cast<int32_t>(rows), rows, pt.k1 - pt.k0, n_heads, descale_q,
-                         descale_k, descale_v, softmax_scale, pt.causal, out8 + r0 * orow, 0,
-                         lse ? lse + r0 : nullptr, lse_stride};
-      st = mla::prefill_launch(a, s);
-      if (st != MLA_OK) return st;
-      continue;
-    }
-    // all parts of this query chunk in ONE launch (fp32 partials in the workspace),
-    // non-causal segments first (the plan lists the causal diagonal last), merged by the
-    // launch itself into the chunk's output rows
-    if (!counters_zeroed) {
-      st = mla::zero_ints(counters, counter_bytes(rows_max, n_heads) / 4, s);
-      if (st != MLA_OK) return st;
-      counters_zeroed = true;
-    }
-    mla::PrefillSegment segs[kMaxParts];
-    for (int i = 0; i < n; ++i) {
-      const Part& pt = parts[i];
-      segs[i] = mla::PrefillSegment{pt.k0, static_cast<int32_t>(pt.k1 - pt.k0), pt.causal,
-                                    ws + i * out_part,
-                                    reinterpret_cast<float*>(lse_ws + i * lse_part)};
-    }
-    mla::PrefillArgs a{q8 + r0 * qrow, k8, v8, nullptr, nullptr, 1, static_cast<int32_t>(rows),
-                       rows, lk, n_heads, descale_q, descale_k, descale_v, softmax_scale, 0,
-                       out8 + r0 * orow, 1, lse ? lse + r0 : nullptr, lse_stride, rows, counters};
-    st = mla::prefill_launch_segments(a, segs, n, s);
+extern "C" int mla_fp8_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                               int64_t lq, int64_t lk, int32_t n_heads,
+                                               const float* descale_q, const float* descale_k,
+                                               const float* descale_v, float softmax_scale,
+                                               int32_t seg_len, int32_t causal, void* out,
+                                               float* lse, int64_t lse_stride, void* stream) {
+  int64_t n_max = 0;
+  int st = check_call(q, k, v, lq, lk, n_heads, descale_q, descale_k, descale_v, softmax_scale,
+                      seg_len, causal, out, lse, lse_stride, &n_max);
+  if (st != MLA_OK || lq == 0) return st == MLA_OK ? mla::ok() : st;
+  // the most query rows per launch whose partials fit the scratch: the whole query chunk,
+  // else a multiple of the prefill's row tile
+  const int64_t chunk = std::min<int64_t>(seg_len, lq);
+  int64_t rows = chunk;
+  if (layout_bytes(n_max, rows, n_heads) > kScratchBytes) {
+    const int64_t tile = mla::prefill_rows_per_block();
+    rows = (chunk - 1) / tile * tile;
+    while (rows > 0 && layout_bytes(n_max, rows, n_heads) > kScratchBytes) rows -= tile;
+    if (rows <= 0)
+      return mla::fail(MLA_ERR_UNSUPPORTED,
+                       "%lld parts of %lld rows x %d heads need %lld bytes of partials; the "
+                       "scratch holds %lld",
+                       static_cast<long long>(n_max), static_cast<long long>(std::min(chunk, tile)),
+                       n_heads, static_cast<long long>(layout_bytes(n_max, std::min(chunk, tile),
+                                                                    n_heads)),
+                       static_cast<long long>(kScratchBytes));
+  }
+  uint8_t* ws = nullptr;
+  if (layout_bytes(n_max, rows, n_heads) > 0) {
+    st = scratch_of_current_device(&ws);
     if (st != MLA_OK) return st;
   }
-  return mla::ok();
+  return run_plan(static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
+                  static_cast<const uint8_t*>(v), lq, lk, n_heads, descale_q, descale_k, descale_v,
+                  softmax_scale, seg_len, causal, static_cast<uint8_t*>(out), lse, lse_stride, ws,
+                  n_max, rows, static_cast<hipStream_t>(stream));
 }

@@ -289,6 +289,34 @@ int mla_fp8_prefill_chunked(const void* q, const void* k, const void* v, int64_t
 int mla_fp8_chunked_workspace_size(int64_t lq, int64_t lk, int32_t n_heads, int32_t seg_len,
                                    int32_t causal, uint64_t* bytes);
 
+/* Device scratch held by the library for mla_fp8_prefill_chunked_noalloc, per GPU. */
+#define MLA_FP8_NOALLOC_SCRATCH_BYTES (64ll * 1024 * 1024)
+
+/*
+ * mla_fp8_prefill_chunked for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, the same plan and arithmetic. Its fp32 partials,
+ * partial LSEs and merge counters live in a library-owned device array of
+ * MLA_FP8_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs on holds until
+ * the process ends; the call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine). The scratch of the current device (hipGetDevice, which must be the
+ * device of `stream`) is looked up on the first call on that device.
+ *   When a query chunk's partials do not fit the scratch, its rows are processed in
+ *   several launches of a multiple of 256 rows each (every row's result is computed the
+ *   same way; only the grouping of adjacent context segments may differ). A plan whose
+ *   partials for 256 rows do not fit (64 MiB < parts * 256 * n_heads * 516 bytes, e.g.
+ *   more than 42 parts at 12 heads) returns MLA_ERR_UNSUPPORTED.
+ *   The merge counters are cleared at the start of every call. All calls on one GPU
+ *   share its scratch: calls that overlap in time on one GPU (several streams or host
+ *   threads) race and give wrong results.
+ *   Errors as for mla_fp8_prefill_chunked; MLA_ERR_HIP if the scratch cannot be found.
+ */
+int mla_fp8_prefill_chunked_noalloc(const void* q, const void* k, const void* v, int64_t lq,
+                                    int64_t lk, int32_t n_heads, const float* descale_q,
+                                    const float* descale_k, const float* descale_v,
+                                    float softmax_scale, int32_t seg_len, int32_t causal,
+                                    void* out, float* lse, int64_t lse_stride, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host-only helpers (no device access; usable without a GPU)                */
 /* ------------------------------------------------------------------------ */
