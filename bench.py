@@ -344,6 +344,22 @@ def main(argv=None):
             f"{rows} rows: {merge_ms * 1e3:.1f} us ({merge_bytes / merge_ms / 1e6:.0f} GB/s)")
     else:
         kernels["prefill_ms"] = round(prefill_ms, 4)
+        # the PV build variants of the FP8 prefill (same inputs, one launch each)
+        pv = {}
+        for mode, variant in ((1, "P in one E4M3 term, FP8 MFMA"),
+                              (2, "P in two E4M3 terms, FP8 MFMA")):
+            path = B.pv_variant_path(mode)
+            if not os.path.exists(path):
+                continue
+            with B.use_library(path):
+                prefill_single()
+                v_ms, _ = event_ms(torch, prefill_single, reps, stream)
+            pv[f"pv{mode}"] = {"what": variant, "prefill_ms": round(v_ms, 4),
+                               "TFLOPs": round(flop / (v_ms * 1e-3) / 1e12, 2)}
+            log(f"[bench] PV variant {mode} ({variant}): {v_ms:.3f} ms = "
+                f"{flop / (v_ms * 1e-3) / 1e12:.1f} TFLOP/s")
+        if pv:
+            kernels["pv_variants"] = pv
         if not wl.causal and wl.batch == 1:
             # split-KV: the same non-causal chunk through the chunked call, one launch over
             # 16384-key segments that merges its own partials

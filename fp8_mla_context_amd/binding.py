@@ -9,13 +9,14 @@ Names mirror the C ABI in ``include/mla_fp8.h``.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Sequence
 
 import numpy as np
 
-from .build import LIB_PATH
+from .build import LIB_PATH, variant_path
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARGUMENT = 1
@@ -91,21 +92,42 @@ def lib_path() -> str:
     return os.environ.get("MLA_FP8_LIB", LIB_PATH)
 
 
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m fp8_mla_context_amd.build`")
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
 def lib() -> ctypes.CDLL:
     """Load the library once; raise if it has not been built."""
     global _LIB
     if _LIB is None:
-        path = lib_path()
-        if not os.path.exists(path):
-            raise RuntimeError(
-                f"{path} is missing: build it with `python -m fp8_mla_context_amd.build`")
-        handle = ctypes.CDLL(path)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _LIB = handle
+        _LIB = _load(lib_path())
     return _LIB
+
+
+def pv_variant_path(mode: int) -> str:
+    """The build variant of the FP8 prefill's PV arithmetic: 0 the default library (P and
+    V in bf16 on the bf16 MFMA), 1 one E4M3 term of P, 2 two E4M3 terms (FP8 MFMA)."""
+    return variant_path({0: "", 1: "_pv1", 2: "_pv2"}[mode], lib_path())
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Route this module's calls to another build of the library (same exports) inside
+    the block, e.g. a PV variant; the default library is restored afterwards."""
+    global _LIB
+    saved = _LIB
+    _LIB = _load(path)
+    try:
+        yield _LIB
+    finally:
+        _LIB = saved
 
 
 def status_string(status: int) -> str:

@@ -84,10 +84,23 @@ constexpr int kVTile = kBN * kVStride;
 // rows 144 bytes apart, so the 16-byte reads of 16 consecutive dims hit distinct banks
 constexpr int kVtStride = 144;
 constexpr int kVtBytes = kDv * kVtStride;
-constexpr int kLdsBytes = 2 * (kKTile + kVTile + kVtBytes);  // 79872: two workgroups per CU
+// PV arithmetic, a build option: 0 (default) P rounded once to bf16 and V converted to
+// bf16 in LDS, on v_mfma_f32_32x32x16_bf16; 1: P' = 2^8 P rounded once to E4M3 (one
+// term) and V used as its FP8 codes, on the FP8 MFMA; 2: P' in two E4M3 terms
+// (hi + lo, both summed into O) on the FP8 MFMA.
+#ifndef MLA_PV_MODE
+#define MLA_PV_MODE 0
+#endif
+constexpr int kPvMode = MLA_PV_MODE;
+static_assert(kPvMode >= 0 && kPvMode <= 2, "MLA_PV_MODE is 0, 1 or 2");
+constexpr bool kPvFp8 = kPvMode != 0;
+constexpr int kLdsBytes =  // bf16 PV: 79872 (two workgroups per CU)
+    kPvFp8 ? 2 * (kKTile + kVTile) : 2 * (kKTile + kVTile + kVtBytes);
 constexpr float kLn2 = 0.69314718055994530942f;
-// P = 2^(logit*log2e - m) <= 2^kRescaleSlack is a bf16 operand; the slack only bounds O.
-constexpr float kRescaleSlack = 8.0f;
+// P = 2^(logit*log2e - m) <= 2^kRescaleSlack. As a bf16 operand the slack only bounds O;
+// the E4M3 operand is P' = 2^8 P <= 2^8.75 < 448, and small weights stay clear of the
+// E4M3 subnormals.
+constexpr float kRescaleSlack = kPvFp8 ? 0.75f : 8.0f;
 
 struct PrefillParams {
   const uint8_t* q;
@@ -432,9 +445,16 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
 
   // prologue: K(0), V(0), K(1) in LDS, S of tile 0 computed, the V^T buffer that
   // iteration 0 reads zeroed (it multiplies a zero P: no uninitialised LDS reaches an MFMA)
-  for (int i = tid; i < kVtBytes / 16; i += kThreads)
-    reinterpret_cast<uint4*>(vtbuf(1))[i] = make_uint4(0, 0, 0, 0);
-  if (n_tiles > 0) { issue(0, true); issue(0, false); }
+  if constexpr (kPvFp8) {
+    // FP8 PV reads the FP8 V tile of the previous iteration: V buffer 1 stands for tile -1
+    for (int i = tid; i < kVTile / 16; i += kThreads)
+      reinterpret_cast<uint4*>(vbuf(1))[i] = make_uint4(0, 0, 0, 0);
+    if (n_tiles > 0) issue(0, true);
+  } else {
+    for (int i = tid; i < kVtBytes / 16; i += kThreads)
+      reinterpret_cast<uint4*>(vtbuf(1))[i] = make_uint4(0, 0, 0, 0);
+    if (n_tiles > 0) { issue(0, true); issue(0, false); }
+  }
   if (n_tiles > 1) issue(1, true);
   wait_vmcnt(0);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the zero stores have landed
@@ -647,12 +667,189 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     block_barrier();
   };
 
+  // ---- FP8 PV (build option). The 32-byte A operand of dim block db is read with four
+  // transposed reads from the FP8 V tile; its byte j = 16 b2 + 4 q + i is key
+  // 32 b2 + 8 q + 4 g + i, which is also the key of byte 4 w + i (w = 4 b2 + q) of the
+  // lane's P operand: registers 4 q .. 4 q + 3 of S block b2.
+  auto vt_operand = [&](const uint8_t* vl, int db) {
+    const uint8_t* vp = vl + (vt_off ^ (db << 5));
+    const v2i r0 = read_tr8(vp);
+    const v2i r1 = read_tr8(vp + 16 * kVStride);
+    const v2i r2 = read_tr8(vp + 32 * kVStride);
+    const v2i r3 = read_tr8(vp + 48 * kVStride);
+    return v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+  };
+  // Softmax of group w (4 keys) into E4M3 operand bytes 4 w .. 4 w + 3.
+  //  one term:  P' = 2^(c s - m + 8), rounded to E4M3 (nearest even); the row sum adds
+  //             the fp32 P'.
+  //  two terms: P = 2^(c s - m) rounded toward zero to f16. The f16 bit pattern of P read
+  //             at bits 7..14 is the E4M3 code of 256 P with its mantissa truncated to 3
+  //             bits (the exponent biases differ by 8 and f16 subnormals map onto E4M3
+  //             subnormals): the hi term is a shift and a byte permute. lo = P - hi is
+  //             exact in f16 and is rounded to 3 mantissa bits (half away from zero) by
+  //             adding 2^6 at bit 0 before the same extraction, so hi + lo is 256 P within
+  //             2^-7 relative. The row sum adds the f16 P (scaled by 256 at the end).
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 ones_h2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  auto softmax_group = [&](const v16f(&sc)[2], float nb, int w, v8i& phi, v8i& plo) {
+    const int b2 = w >> 2, r = 4 * (w & 3);
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[b2][r], c, nb));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[b2][r + 1], c, nb));
+    const float e2 = __builtin_amdgcn_exp2f(fmaf(sc[b2][r + 2], c, nb));
+    const float e3 = __builtin_amdgcn_exp2f(fmaf(sc[b2][r + 3], c, nb));
+    if constexpr (kPvMode == 1) {
+      l_run += (e0 + e1) + (e2 + e3);
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, v, true);
+      phi[w] = v;
+      asm volatile("" ::"v"(phi[w]), "v"(l_run));
+    } else {
+      const h2 p01 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(e0, e1));
+      const h2 p23 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(e2, e3));
+      l_run = __builtin_amdgcn_fdot2(p01, ones_h2, l_run, false);
+      l_run = __builtin_amdgcn_fdot2(p23, ones_h2, l_run, false);
+      const uint32_t u01 = __builtin_bit_cast(uint32_t, p01);
+      const uint32_t u23 = __builtin_bit_cast(uint32_t, p23);
+      // (u << 1) moves bits 7..14 of each half to bytes 1 and 3
+      phi[w] = static_cast<int>(__builtin_amdgcn_perm(u23 << 1, u01 << 1, 0x07050301u));
+      const h2 lo01 = p01 - __builtin_bit_cast(h2, u01 & 0xFF80FF80u);
+      const h2 lo23 = p23 - __builtin_bit_cast(h2, u23 & 0xFF80FF80u);
+      const uint32_t q01 = (__builtin_bit_cast(uint32_t, lo01) << 1) + 0x00800080u;
+      const uint32_t q23 = (__builtin_bit_cast(uint32_t, lo23) << 1) + 0x00800080u;
+      plo[w] = static_cast<int>(__builtin_amdgcn_perm(q23, q01, 0x07050301u));
+      asm volatile("" ::"v"(phi[w]), "v"(plo[w]), "v"(l_run));
+    }
+  };
+  // One iteration with FP8 PV: K(it+2) and V(it) are loaded (V(it) into the buffer that
+  // V(it-2) left; PV of tile it-1 reads V(it-1) as FP8 codes, V buffer 1 zeroed for
+  // tile -1). The 6 S MFMAs of tile it+1 with the mask and row max of tile it between
+  // them, then the PV MFMAs of tile it-1 (4 dim blocks, one or two terms) with the
+  // softmax groups of tile it between them.
+  auto step_fp8 = [&](int it, v16f(&s_c)[2], v16f(&s_n)[2], const v8i& phi_p, const v8i& plo_p,
+                      v8i& phi_c, v8i& plo_c) {
+    const bool active = it < wave_iters;
+    const uint8_t* kl = kbuf(it + 1);
+    const uint8_t* vl = vbuf(it - 1);
+    v8i va[4];
+    v8i ka;
+    if (active) {
+      va[0] = vt_operand(vl, 0);
+      va[1] = vt_operand(vl, 1);
+      ka = k_operand(kl, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + 2 < n_tiles) issue(it + 2, true);
+    if (it < n_tiles) issue(it, false);
+
+    if (active) {
+      const int kt = it * kBN;
+      const bool need_mask =
+          it >= wave_tiles || (kt + kBN > Lk) || (causal && kt + kBN - 1 > wrow0 + off);
+      const v16f zero = {};
+      s_n[0] = mfma_f8(ka, qf[0], zero);
+      ka = k_operand(kl, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (need_mask) {
+        asm volatile("" ::: "memory");
+        const bool all = it >= wave_tiles;
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt + 32 * b2 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (all || key >= Lk || (causal && key > my_row + off)) s_c[b2][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = vmax3(mx, s_c[0][r], s_c[0][r + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      s_n[1] = mfma_f8(ka, qf[0], zero);
+      ka = k_operand(kl, 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = vmax3(mx, s_c[1][r], s_c[1][r + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      s_n[0] = mfma_f8(ka, qf[1], s_n[0]);
+      ka = k_operand(kl, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float m_tile = mx * c;
+      const bool rescale = __any(m_tile > m_run + kRescaleSlack);
+      float alpha = 1.f;
+      if (rescale) {
+        asm volatile("" ::: "memory");
+        const float m_new = fmaxf(m_run, m_tile);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      // one term: P' = 2^8 P directly from the exponent
+      const float nb = ((m_run == -INFINITY) ? 0.f : -m_run) + (kPvMode == 1 ? 8.f : 0.f);
+      __builtin_amdgcn_sched_barrier(0);
+      s_n[1] = mfma_f8(ka, qf[1], s_n[1]);
+      ka = k_operand(kl, 4);
+      va[2] = vt_operand(vl, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      s_n[0] = mfma_f8(ka, qf[2], s_n[0]);
+      ka = k_operand(kl, 5);
+      va[3] = vt_operand(vl, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      s_n[1] = mfma_f8(ka, qf[2], s_n[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kPvMode == 1) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          o[db] = mfma_f8(va[db], phi_p, o[db]);
+          __builtin_amdgcn_sched_barrier(0);
+          softmax_group(s_c, nb, 2 * db, phi_c, plo_c);
+          softmax_group(s_c, nb, 2 * db + 1, phi_c, plo_c);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        // hi and lo terms alternate between dim blocks: consecutive MFMAs write
+        // different accumulators
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int db = 2 * (j >> 2) + (j & 1);
+          o[db] = mfma_f8(va[db], (j & 2) ? plo_p : phi_p, o[db]);
+          __builtin_amdgcn_sched_barrier(0);
+          softmax_group(s_c, nb, j, phi_c, plo_c);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (rescale) {
+        asm volatile("" : "+v"(alpha)::"memory");
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+    }
+    wait_vmcnt(0);  // K(it+2) and V(it) have landed
+    block_barrier();
+  };
+
   v16f s_alt[2];
-  v8bf pb_a[4] = {v8bf{}, v8bf{}, v8bf{}, v8bf{}};
-  v8bf pb_b[4] = {v8bf{}, v8bf{}, v8bf{}, v8bf{}};
-  for (int it = 0; it <= n_tiles; it += 2) {
-    step(it, s_cur, s_alt, pb_a, pb_b);
-    if (it + 1 <= n_tiles) step(it + 1, s_alt, s_cur, pb_b, pb_a);
+  if constexpr (kPvFp8) {
+    v8i phi_a = {}, plo_a = {}, phi_b = {}, plo_b = {};
+    for (int it = 0; it <= n_tiles; it += 2) {
+      step_fp8(it, s_cur, s_alt, phi_a, plo_a, phi_b, plo_b);
+      if (it + 1 <= n_tiles) step_fp8(it + 1, s_alt, s_cur, phi_b, plo_b, phi_a, plo_a);
+    }
+    l_run *= (kPvMode == 2) ? 256.f : 1.f;  // l in units of P' = 2^8 P
+  } else {
+    v8bf pb_a[4] = {v8bf{}, v8bf{}, v8bf{}, v8bf{}};
+    v8bf pb_b[4] = {v8bf{}, v8bf{}, v8bf{}, v8bf{}};
+    for (int it = 0; it <= n_tiles; it += 2) {
+      step(it, s_cur, s_alt, pb_a, pb_b);
+      if (it + 1 <= n_tiles) step(it + 1, s_alt, s_cur, pb_b, pb_a);
+    }
   }
 
   // epilogue: this lane holds row my_row, dims 32*db + 8*(r/4) + 4*g + r%4
@@ -698,7 +895,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     if (g == 0 && lse_ptr != nullptr) {
       float* lp = lse_ptr + static_cast<int64_t>(h) * (kNSeg > 1 ? p.seg_lse_stride : p.lse_stride) +
                   q0 + my_row;
-      const float lv = (l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      const float lv =
+          (l_tot > 0.f) ? (m_run + __log2f(l_tot) - (kPvFp8 ? 8.f : 0.f)) * kLn2 : -INFINITY;
       if (kNSeg > 1 && p.counters != nullptr)
         __hip_atomic_store(lp, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else
