@@ -255,9 +255,11 @@ __device__ __forceinline__ void merge_on_last_arrival(const PrefillParams& p,
   }
 }
 
-template <int kNSeg>
+// kPv (= MLA_PV_MODE) only names the build variant, so that kernel traces keep them apart
+template <int kNSeg, int kPv>
 __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(PrefillParams p,
                                                                         SegTable<kNSeg> st) {
+  static_assert(kPv == kPvMode, "the PV arithmetic is chosen at build time");
   // K tile t, FP8 V tile t and bf16 V^T of tile t each in buffer t % 2 of their kind
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
 
@@ -973,7 +975,7 @@ int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   if (blocks >= (1ll << 31)) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
   prm.xcd_order = (a.batch == 1 && a.n_heads % 4 == 0 && n_m % 2 == 0) ? 1 : 0;
   SegTable<1> none{};
-  hipLaunchKernelGGL(prefill_fp8_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+  hipLaunchKernelGGL((prefill_fp8_kernel<1, kPvMode>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
                      0, stream, prm, none);
   return check_launch("prefill_fp8_kernel");
 }
@@ -1002,7 +1004,7 @@ int prefill_launch_segments(const PrefillArgs& a, const PrefillSegment* segs, in
   }
   const int64_t blocks = n_m * n * a.n_heads;
   if (blocks >= (1ll << 31)) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
-  hipLaunchKernelGGL(prefill_fp8_kernel<kMaxPrefillSegments>, dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((prefill_fp8_kernel<kMaxPrefillSegments, kPvMode>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kThreads), 0, stream, prm, tab);
   return check_launch("prefill_fp8_kernel");
 }
