@@ -21,10 +21,11 @@
 //    weight stays resident in each XCD's L2.
 //  * The 512-deep reduction runs in 16 chunks of 32; chunk c's weight rows (256 x 64 B)
 //    and latent rows (128 x 64 B) are DMA'd (global_load_lds_dwordx4) into LDS buffer
-//    c % 2, rows padded to 80 bytes (the 16-byte operand reads of 16 consecutive rows hit
-//    distinct banks), one chunk ahead of their use. Two workgroups share a CU.
-//  * Epilogue: fp32 -> bf16 (v_cvt_pk_bf16_f32, nearest even) -> E4M3 code (the exact
-//    quantizer of the standalone kernel; it dominates the kernel's VALU time). The codes
+//    c % 3, two chunks ahead of their use, the four 16-byte pieces of a row XOR-swizzled
+//    so that the operand reads of 16 consecutive rows hit distinct banks. Two workgroups
+//    share a CU.
+//  * Epilogue: fp32 -> bf16 (v_cvt_pk_bf16_f32, nearest even) -> E4M3 code, looked up in
+//    per-head tables of the exact quantizer's codes built in LDS at the start. The codes
 //    pass through LDS so that each thread stores whole 16-byte pieces of k8 / v8 rows;
 //    the rope part is quantized with the head's key scale, 16 values per thread. The
 //    bf16 K and V can be written as well (for a BF16 attention path).
@@ -50,20 +51,36 @@ constexpr int kThreads = 512;       // 8 waves
 constexpr int kTM = 128;            // tokens per workgroup
 constexpr int kKC = 32;             // reduction chunk
 constexpr int kNChunks = kLatent / kKC;
-constexpr int kRowBytes = 80;       // 64 data bytes + 16 pad per LDS row
-constexpr int kWRegion = kFeat * kRowBytes;  // 20480
-constexpr int kCRegion = kTM * kRowBytes;    // 10240
-constexpr int kStage = kWRegion + kCRegion;  // 30720
-// Two LDS buffers (60 KB) leave room for two workgroups per CU, so that one workgroup's
-// quantizing epilogue overlaps the other's projection; a chunk is loaded one chunk ahead.
-constexpr int kStages = 2;
+constexpr int kRowBytes = 64;       // one chunk of a row: four 16-byte pieces, swizzled
+constexpr int kWRegion = kFeat * kRowBytes;  // 16384
+constexpr int kCRegion = kTM * kRowBytes;    // 8192
+constexpr int kStage = kWRegion + kCRegion;  // 24576
+// Three LDS buffers (72 KB, chunks loaded two ahead) leave room for two workgroups per
+// CU, so that one workgroup's quantizing epilogue overlaps the other's projection.
+constexpr int kStages = 3;
 constexpr int kWgPerCu = 2;
-constexpr int kWInstr = kFeat * 5 / 64;  // 20 DMA instructions (5 slots per row)
-constexpr int kCInstr = kTM * 5 / 64;    // 10
+constexpr int kWInstr = kFeat * 4 / 64;  // 16 DMA instructions (4 pieces per row)
+constexpr int kCInstr = kTM * 4 / 64;    // 8
 constexpr int kInstr = kWInstr + kCInstr;
-constexpr int kPerWave = (kInstr + 7) / 8;  // 4
+constexpr int kPerWave = (kInstr + 7) / 8;  // 3
+// piece p of row r sits at position p ^ ((r >> 2) & 3): the 16-byte operand reads of 16
+// consecutive rows (same piece) then cover all 64 banks
+__device__ __forceinline__ int piece_pos(int row, int piece) { return piece ^ ((row >> 2) & 3); }
 constexpr int kCodeStride = kFeat + 16;  // LDS bytes per token row of the code tile
 static_assert(kStages * kStage >= kTM * kCodeStride, "the code tile reuses the stage buffers");
+
+// Code tables. For a descale d in [2^E, 2^(E+1)), a bf16 magnitude below binade
+// e_lo = E + 117 is under 2^(E-10), so its quotient is under 2^-10 (half the smallest
+// subnormal): code 0. From binade e_lo + 20 = E + 137 up it is at least 2^(E+10), so the
+// quotient exceeds 512: saturated (0x7E). The 20 binades between hold every other code.
+// Table entry 0 is 0, entry 1 + ((e - e_lo) << 7 | mantissa) the code of that magnitude
+// (from quant_one, so every lookup equals it), entry 1 + 20 * 128 is 0x7E; the index is
+// the magnitude minus (e_lo << 7), clamped to [-1, 20 * 128], plus one. NaN inputs (above
+// the window) take quant_one itself.
+constexpr int kTabRows = 20;
+constexpr int kTabEntries = kTabRows * 128 + 2;
+constexpr int kTabBytes = (kTabEntries + 15) / 16 * 16;
+constexpr int kLdsBytes = kStages * kStage + 2 * kTabBytes;  // stages, then the K and V tables
 
 struct ProducerParams {
   const uint16_t* c_kv;
@@ -86,8 +103,44 @@ __device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v1
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Entry j of the code table of descale d (r = 1/d, e_lo = ilogb(d) + 117)
+__device__ __forceinline__ uint8_t table_entry(int j, float d, float r, int e_lo) {
+  const int e = e_lo + ((j - 1) >> 7);
+  uint32_t code = 0;
+  if (j == kTabEntries - 1)
+    code = 0x7Eu;
+  else if (j > 0 && e >= 0 && e <= 255)
+    code = quant_one(static_cast<uint32_t>((e << 7) | ((j - 1) & 127)), d, r);
+  return static_cast<uint8_t>(code);
+}
+
+// Codes of 16 bf16 values (w[i] holds elements 2i and 2i+1) through the table of descale
+// d (base = e_lo << 7); byte k of the result is the code of element k. A group holding a
+// NaN anywhere in the wave takes quant16.
+__device__ __forceinline__ uint4 quant16_tab(const uint32_t (&w)[8], const uint8_t* tab,
+                                             int base, float d, float r) {
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx = max(mx, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  if (__builtin_expect(__any(mx > 0x7F80u), 0)) return quant16(w, d, r);
+  auto look = [&](uint32_t mag) {
+    const int idx = min(max(static_cast<int>(mag) - base, -1), kTabRows * 128) + 1;
+    return static_cast<uint32_t>(tab[idx]);
+  };
+  uint32_t out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t w0 = w[2 * k], w1 = w[2 * k + 1];
+    const uint32_t c = look(w0 & 0x7FFFu) | (look((w0 >> 16) & 0x7FFFu) << 8) |
+                       (look(w1 & 0x7FFFu) << 16) | (look((w1 >> 16) & 0x7FFFu) << 24);
+    // the sign bits: the high byte of each bf16 element
+    out[k] = c | (__builtin_amdgcn_perm(w1, w0, 0x07050301u) & 0x80808080u);
+  }
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(ProducerParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,8 +157,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
   const int n_tok = static_cast<int>(min<int64_t>(kTM, p.n_tokens - t0));  // >= 1
 
   // DMA slots: instruction i (i = wave + 8 j) writes 16-byte LDS slots 64 i + lane of the
-  // stage; slots 0..1279 are weight rows (5 per row: 4 data + 1 pad that repeats the last
-  // piece), then 640 slots of latent rows (rows past the last token repeat it).
+  // stage; slots 0..1023 are weight rows (4 per row), then 512 slots of latent rows (rows
+  // past the last token repeat it). Slot position q of row r holds piece q ^ ((r >> 2) & 3).
   const uint8_t* w_base = reinterpret_cast<const uint8_t*>(p.w) +
                           static_cast<int64_t>(h) * kFeat * kLatent * 2;
   const uint8_t* c_base = reinterpret_cast<const uint8_t*>(p.c_kv) + t0 * p.c_stride * 2;
@@ -114,8 +167,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
   for (int j = 0; j < kPerWave; ++j) {
     const int i = min(wave + 8 * j, kInstr - 1);
     const int s = (i < kWInstr ? i * 64 : (i - kWInstr) * 64) + lane;
-    const int row = s / 5;
-    const int piece = min(s - 5 * row, 3);
+    const int row = s >> 2;
+    const int piece = piece_pos(row, s & 3);  // the swizzle is its own inverse
     if (i < kWInstr)
       dma_off[j] = static_cast<uint32_t>(row * kLatent * 2 + 16 * piece);
     else
@@ -160,6 +213,17 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
   // c + 1 must have landed, so the loads of chunks c + 2 .. next - 1 may stay in flight
   int next = 0;
   for (; next < kStages - 1; ++next) issue(next);
+  // The code tables of this head (K then V, 2 kTabEntries entries) are filled during the
+  // first chunks, entry tid + kThreads c in chunk c, in VALU time the loop leaves idle;
+  // descales outside [2^-126, 2^126] skip them (every code then comes from quant16).
+  const float dk = p.dk[h], dv = p.dv[h];
+  const bool tab_ok = dk >= 0x1p-126f && dk <= 0x1p126f && dv >= 0x1p-126f && dv <= 0x1p126f;
+  uint8_t* tab_k = lds + kStages * kStage;
+  uint8_t* tab_v = tab_k + kTabBytes;
+  const float rk = 1.0f / dk, rv = 1.0f / dv;
+  const int elo_k = ilogbf(dk) + 117, elo_v = ilogbf(dv) + 117;
+  constexpr int kTabChunks = (2 * kTabEntries + kThreads - 1) / kThreads;
+  static_assert(kTabChunks <= kNChunks, "the tables are filled within the loop");
   wait_vmcnt(n_mine * (next - 1));
   block_barrier();
   for (int c = 0; c < kNChunks; ++c) {
@@ -169,20 +233,31 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
     for (int ks = 0; ks < 2; ++ks) {
       v8bf a[2], b[2];
 #pragma unroll
-      for (int fb = 0; fb < 2; ++fb)
-        a[fb] = *reinterpret_cast<const v8bf*>(stage + (64 * fq + 32 * fb + col) * kRowBytes +
-                                                32 * ks + 16 * g);
+      for (int fb = 0; fb < 2; ++fb) {
+        const int row = 64 * fq + 32 * fb + col;
+        a[fb] = *reinterpret_cast<const v8bf*>(stage + row * kRowBytes +
+                                                16 * piece_pos(row, 2 * ks + g));
+      }
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-        b[tb] = *reinterpret_cast<const v8bf*>(stage + kWRegion +
-                                                (64 * tq + 32 * tb + col) * kRowBytes + 32 * ks +
-                                                16 * g);
+      for (int tb = 0; tb < 2; ++tb) {
+        const int row = 64 * tq + 32 * tb + col;
+        b[tb] = *reinterpret_cast<const v8bf*>(stage + kWRegion + row * kRowBytes +
+                                                16 * piece_pos(row, 2 * ks + g));
+      }
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) acc[fb][tb] = mfma_bf16(a[fb], b[tb], acc[fb][tb]);
     }
+    if (tab_ok && c < kTabChunks) {
+      const int i = tid + kThreads * c;
+      if (i < kTabEntries)
+        tab_k[i] = table_entry(i, dk, rk, elo_k);
+      else if (i < 2 * kTabEntries)
+        tab_v[i - kTabEntries] = table_entry(i - kTabEntries, dv, rv, elo_v);
+    }
     wait_vmcnt(next > c + 2 ? n_mine * (next - c - 2) : 0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the table stores too
     block_barrier();
   }
 
@@ -190,9 +265,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
   // 64 fq + 32 fb + 8 q + 4 g + (0..3), q = 0..3. Their codes go to an LDS tile of 128
   // token rows (kCodeStride bytes apart: consecutive tokens start 4 banks apart), then
   // out in 16-byte pieces.
-  const float dk = p.dk[h], dv = p.dv[h];
   const float d = fq < 2 ? dk : dv;  // features 0..127 are k_nope, 128..255 v
-  const float rr = 1.0f / d;
+  const float rr = fq < 2 ? rk : rv;
+  const uint8_t* tab = fq < 2 ? tab_k : tab_v;
+  const int base = (fq < 2 ? elo_k : elo_v) << 7;
   const int64_t kst = static_cast<int64_t>(H) * 192, vst = static_cast<int64_t>(H) * kDv;
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
@@ -211,7 +287,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
             uint32_t,
             __builtin_convertvector(v2f{acc[fb][tb][4 * q + 2], acc[fb][tb][4 * q + 3]}, v2bf));
       }
-      const uint4 cd = quant16(pr, d, rr);
+      const uint4 cd = tab_ok ? quant16_tab(pr, tab, base, d, rr) : quant16(pr, d, rr);
       const uint32_t cw[4] = {cd.x, cd.y, cd.z, cd.w};  // word q: codes of (q, 0..3)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -245,7 +321,8 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
   if (pe_tok < n_tok) {
     const uint32_t w[8] = {pe_a.x, pe_a.y, pe_a.z, pe_a.w, pe_b.x, pe_b.y, pe_b.z, pe_b.w};
     const int64_t o = (t0 + pe_tok) * kst + h * 192 + kNope + 16 * pe_pc;
-    *reinterpret_cast<uint4*>(p.k8 + o) = quant16(w, dk, 1.0f / dk);
+    *reinterpret_cast<uint4*>(p.k8 + o) =
+        tab_ok ? quant16_tab(w, tab_k, elo_k << 7, dk, rk) : quant16(w, dk, rk);
     if (p.kb != nullptr) {
       *reinterpret_cast<uint4*>(p.kb + o) = pe_a;
       *reinterpret_cast<uint4*>(p.kb + o + 8) = pe_b;
