@@ -25,10 +25,13 @@
 //    so that the operand reads of 16 consecutive rows hit distinct banks. Two workgroups
 //    share a CU.
 //  * Epilogue: fp32 -> bf16 (v_cvt_pk_bf16_f32, nearest even) -> E4M3 code, looked up in
-//    per-head tables of the exact quantizer's codes built in LDS at the start. The codes
-//    pass through LDS so that each thread stores whole 16-byte pieces of k8 / v8 rows;
-//    the rope part is quantized with the head's key scale, 16 values per thread. The
-//    bf16 K and V can be written as well (for a BF16 attention path).
+//    per-head tables of the exact quantizer's codes, filled in LDS during the first
+//    chunks of the reduction. The codes pass through LDS so that each thread stores
+//    whole 16-byte pieces of k8 / v8 rows, with non-temporal stores: the 126 MB of codes
+//    of a 32K-token call would otherwise push the weight and the shared latent rows out
+//    of L2 (3x the HBM reads). The rope part is quantized with the head's key scale, 16
+//    values per thread. The bf16 K and V can be written as well (for a BF16 attention
+//    path).
 #include "device_common.h"
 #include "e4m3_quant.h"
 #include "mla_internal.h"
@@ -41,6 +44,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kLatent = 512;
 constexpr int kRope = 64;
@@ -313,16 +317,18 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
       const uint4 v = *reinterpret_cast<const uint4*>(lds + tok * kCodeStride + 16 * pc);
       const int64_t t = t0 + tok;
       if (pc < 8)
-        *reinterpret_cast<uint4*>(p.k8 + t * kst + h * 192 + 16 * pc) = v;
+        __builtin_nontemporal_store(__builtin_bit_cast(v4u, v),
+                                    reinterpret_cast<v4u*>(p.k8 + t * kst + h * 192 + 16 * pc));
       else
-        *reinterpret_cast<uint4*>(p.v8 + t * vst + h * kDv + 16 * (pc - 8)) = v;
+        __builtin_nontemporal_store(__builtin_bit_cast(v4u, v),
+                                    reinterpret_cast<v4u*>(p.v8 + t * vst + h * kDv + 16 * (pc - 8)));
     }
   }
   if (pe_tok < n_tok) {
     const uint32_t w[8] = {pe_a.x, pe_a.y, pe_a.z, pe_a.w, pe_b.x, pe_b.y, pe_b.z, pe_b.w};
     const int64_t o = (t0 + pe_tok) * kst + h * 192 + kNope + 16 * pe_pc;
-    *reinterpret_cast<uint4*>(p.k8 + o) =
-        tab_ok ? quant16_tab(w, tab_k, elo_k << 7, dk, rk) : quant16(w, dk, rk);
+    const uint4 cr = tab_ok ? quant16_tab(w, tab_k, elo_k << 7, dk, rk) : quant16(w, dk, rk);
+    __builtin_nontemporal_store(__builtin_bit_cast(v4u, cr), reinterpret_cast<v4u*>(p.k8 + o));
     if (p.kb != nullptr) {
       *reinterpret_cast<uint4*>(p.kb + o) = pe_a;
       *reinterpret_cast<uint4*>(p.kb + o + 8) = pe_b;
