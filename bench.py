@@ -55,6 +55,66 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def record_counters(dirs, workload: str) -> dict:
+    """Build the per-launch counter record of the prefill from rocprofv3 `--pmc` output
+    directories (one per pass, csv format) of a run with --copy-probe-mib 1024, and write
+    it to profiles/prefill_<workload>_counters.json. Counter values are summed over their
+    dimensions per dispatch and averaged over dispatches; FETCH_SIZE and WRITE_SIZE are
+    scaled by what they read for the elementwise probe, which moves 1 GiB each way."""
+    import csv
+    import glob
+    import re as _re
+
+    per = {}  # kernel name -> counter -> list of per-dispatch sums
+    for d in dirs:
+        acc, names = {}, {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    key = (r["Dispatch_Id"], r["Counter_Name"])
+                    acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+                    names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        for (disp, cn), v in acc.items():
+            per.setdefault(names[disp], {}).setdefault(cn, []).append(v)
+    mean = {k: {cn: sum(v) / len(v) for cn, v in d.items()} for k, d in per.items()}
+    pre = [k for k in mean if _re.search(r"prefill_fp8_kernel<1, 0>", k)]  # default PV mode
+    probe = [k for k in mean if "elementwise" in k.lower() and mean[k].get("FETCH_SIZE", 0) > 500000]
+    if len(pre) != 1 or len(probe) != 1:
+        raise SystemExit(f"expected one prefill kernel and one probe kernel, found {pre} / {probe}")
+    v, pv = mean[pre[0]], mean[probe[0]]
+    fetch_scale = round(1048576 / pv["FETCH_SIZE"], 2)
+    write_scale = round(1048576 / pv["WRITE_SIZE"], 2)
+    rec = {
+        "kernel_hash": kernel_source_hash(),
+        "hbm_bytes_per_launch": int(round(v["FETCH_SIZE"] * 1024 * fetch_scale +
+                                          v["WRITE_SIZE"] * 1024 * write_scale)),
+        "fetch_size_kib": v["FETCH_SIZE"],
+        "write_size_kib": v["WRITE_SIZE"],
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "calibration": f"elementwise kernel over 1 GiB uint8: FETCH_SIZE {pv['FETCH_SIZE']:,.0f} KiB, "
+                       f"WRITE_SIZE {pv['WRITE_SIZE']:,.0f} KiB",
+    }
+    if "GRBM_GUI_ACTIVE" in v:
+        rec["gfx_cycles_per_launch"] = int(round(v["GRBM_GUI_ACTIVE"] / 8))
+        rec["gfx_cycles_counter"] = "GRBM_GUI_ACTIVE summed over the 8 XCDs, divided by 8"
+    for cn, key in (("SQ_INSTS_VALU_MFMA_F8", "mfma_f8_instructions"),
+                    ("SQ_INSTS_VALU_MFMA_BF16", "mfma_bf16_instructions"),
+                    ("SQ_INSTS_VALU", "valu_instructions"), ("SQ_INSTS_LDS", "lds_instructions")):
+        if cn in v:
+            rec[key] = v[cn]
+    if "SQ_INSTS_VALU_MFMA_MOPS_F8" in v and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in v:
+        rec["mfma_executed_flop"] = (v["SQ_INSTS_VALU_MFMA_MOPS_F8"] + v["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) * 512
+    for cn, key in (("SQ_VALU_MFMA_BUSY_CYCLES", "mfma_busy_cycles_per_simd"),
+                    ("SQ_VALU_MFMA_COEXEC_CYCLES", "valu_mfma_coexec_cycles_per_simd")):
+        if cn in v:
+            rec[key] = int(round(v[cn] / 1024))  # 256 CUs x 4 SIMDs
+    path = os.path.join(ROOT, "profiles", f"prefill_{workload.lower()}_counters.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def load_counters(kernel_hash: str, workload: str):
     """Per-launch counter record of the prefill (HBM bytes, GPU clock cycles) for this
     workload, if it was taken on the current kernel sources; else an empty dict."""
@@ -191,8 +251,14 @@ def main(argv=None):
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run an elementwise read+write kernel of this size (counter "
                          "calibration and practical HBM roofline)")
+    ap.add_argument("--record-counters", nargs="+", metavar="DIR",
+                    help="no run: build profiles/prefill_<workload>_counters.json from these "
+                         "rocprofv3 --pmc output directories")
     args = ap.parse_args(argv)
 
+    if args.record_counters:
+        print(json.dumps(record_counters(args.record_counters, args.workload), indent=1))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(heads or context segments would shard with no or one exchange step).",
@@ -238,18 +304,21 @@ def main(argv=None):
         need = B.chunked_workspace_size(wl.total_q, wl.total_k, heads, wl.segment_len, wl.causal)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
-    def quant():
-        B.quant_static([q, k, v], descales, outs=codes)
+    # The step goes through the checked calls. Per-kernel event timings use the same calls
+    # prepared once (prepare=True: arguments checked and marshalled, a callable that only
+    # launches), so that the events time the kernels and not the host-side checks.
+    def quant(prepare=False):
+        return B.quant_static([q, k, v], descales, outs=codes, prepare=prepare)
 
-    def prefill_single():
-        B.prefill_varlen(codes[0], codes[1], codes[2], cu_q, cu_k, wl.max_seqlen_q,
-                         wl.max_seqlen_k, descales[0], descales[1], descales[2], wl.softmax_scale,
-                         wl.causal, out=out, lse=lse)
+    def prefill_single(prepare=False):
+        return B.prefill_varlen(codes[0], codes[1], codes[2], cu_q, cu_k, wl.max_seqlen_q,
+                                wl.max_seqlen_k, descales[0], descales[1], descales[2],
+                                wl.softmax_scale, wl.causal, out=out, lse=lse, prepare=prepare)
 
-    def prefill_chunked():
-        B.prefill_chunked(codes[0], codes[1], codes[2], descales[0], descales[1], descales[2],
-                          wl.softmax_scale, wl.segment_len, wl.causal, out=out, lse=lse,
-                          workspace=workspace)
+    def prefill_chunked(prepare=False):
+        return B.prefill_chunked(codes[0], codes[1], codes[2], descales[0], descales[1],
+                                 descales[2], wl.softmax_scale, wl.segment_len, wl.causal,
+                                 out=out, lse=lse, workspace=workspace, prepare=prepare)
 
     prefill = prefill_chunked if chunked else prefill_single
 
@@ -280,8 +349,8 @@ def main(argv=None):
     # per-kernel durations with HIP events on the launch stream (torch's current stream)
     stream = torch.cuda.current_stream()
     reps = max(args.steps, 3)
-    quant_ms, _ = event_ms(torch, quant, reps, stream)
-    prefill_ms, prefill_min = event_ms(torch, prefill, reps, stream)
+    quant_ms, _ = event_ms(torch, quant(prepare=True), reps, stream)
+    prefill_ms, prefill_min = event_ms(torch, prefill(prepare=True), reps, stream)
     achieved = flop / (prefill_ms * 1e-3) / 1e12
     what = "chunked prefill (all segments + merges)" if chunked else "prefill"
     log(f"[bench] event timing: quant {quant_ms * 1e3:.1f} us ({quant_bytes / quant_ms / 1e6:.0f} GB/s), "
@@ -307,7 +376,7 @@ def main(argv=None):
         kernels["chunked_prefill_ms"] = round(prefill_ms, 4)
         kernels["pipeline_ms"] = round(quant_ms + prefill_ms, 4)
         # the same attention as one unsegmented bottom-right causal call
-        single_ms, _ = event_ms(torch, prefill_single, reps, stream)
+        single_ms, _ = event_ms(torch, prefill_single(prepare=True), reps, stream)
         kernels["unsegmented_prefill_ms"] = round(single_ms, 4)
         kernels["unsegmented_TFLOPs"] = round(flop / (single_ms * 1e-3) / 1e12, 2)
         # the plan as the workload states it (every context segment its own call, bf16
@@ -334,8 +403,8 @@ def main(argv=None):
         lses = [torch.randn((heads, rows), device="cuda", generator=gen) for _ in range(n_parts)]
         m_out = torch.empty_like(parts[0])
         m_lse = torch.empty_like(lses[0])
-        merge_ms, _ = event_ms(torch, lambda: B.merge_lse(parts, lses, out=m_out, lse_out=m_lse),
-                               reps, stream)
+        merge_ms, _ = event_ms(torch, B.merge_lse(parts, lses, out=m_out, lse_out=m_lse,
+                                                  prepare=True), reps, stream)
         merge_bytes = (n_parts + 1) * rows * heads * (128 * 2 + 4)
         kernels["merge_lse"] = {"partials": n_parts, "rows": rows, "us": round(merge_ms * 1e3, 2),
                                 "bytes": merge_bytes,
@@ -352,8 +421,9 @@ def main(argv=None):
             if not os.path.exists(path):
                 continue
             with B.use_library(path):
-                prefill_single()
-                v_ms, _ = event_ms(torch, prefill_single, reps, stream)
+                call = prefill_single(prepare=True)
+                call()
+                v_ms, _ = event_ms(torch, call, reps, stream)
             pv[f"pv{mode}"] = {"what": variant, "prefill_ms": round(v_ms, 4),
                                "TFLOPs": round(flop / (v_ms * 1e-3) / 1e12, 2)}
             log(f"[bench] PV variant {mode} ({variant}): {v_ms:.3f} ms = "
@@ -369,9 +439,10 @@ def main(argv=None):
                              dtype=torch.uint8, device="cuda")
             s_out = torch.empty_like(out)
             s_lse = torch.empty_like(lse)
-            split_ms, _ = event_ms(torch, lambda: B.prefill_chunked(
+            split_ms, _ = event_ms(torch, B.prefill_chunked(
                 codes[0], codes[1], codes[2], descales[0], descales[1], descales[2],
-                wl.softmax_scale, seg, False, out=s_out, lse=s_lse, workspace=ws), reps, stream)
+                wl.softmax_scale, seg, False, out=s_out, lse=s_lse, workspace=ws, prepare=True),
+                reps, stream)
             kernels["split_kv_chunked"] = {"segment": seg, "ms": round(split_ms, 4),
                                            "TFLOPs": round(flop / (split_ms * 1e-3) / 1e12, 2)}
             log(f"[bench] split-KV over {seg}-key segments (chunked call, merge in the launch): "
@@ -413,9 +484,10 @@ def main(argv=None):
     del cache_bits, w_bits
     pk8 = torch.empty((wl.total_k, heads, 192), dtype=torch.uint8, device="cuda")
     pv8 = torch.empty((wl.total_k, heads, 128), dtype=torch.uint8, device="cuda")
-    prod_ms, _ = event_ms(torch, lambda: B.kv_produce(
-        d_cache[:, :512], d_cache[:, 512:], d_w, descales[1], descales[2], k8=pk8, v8=pv8),
-        reps, stream)
+    prod_call = B.kv_produce(d_cache[:, :512], d_cache[:, 512:], d_w, descales[1], descales[2],
+                             k8=pk8, v8=pv8, prepare=True)
+    prod_call()
+    prod_ms, _ = event_ms(torch, prod_call, reps, stream)
     prod_bytes = wl.total_k * (576 * 2 + heads * 320) + d_w.numel() * 2
     prod_flop = 2.0 * wl.total_k * heads * 256 * 512
     kernels["kv_produce"] = {
@@ -445,7 +517,7 @@ def main(argv=None):
     rec = load_counters(khash, wl.name)
     roofline = {
         "bound": "mfma",
-        "kernel": "prefill_fp8_kernel" + (" (+ merge_lse_kernel, chunked)" if chunked else ""),
+        "kernel": "prefill_fp8_kernel" + (" (segment launches, merge inside)" if chunked else ""),
         "achieved": round(achieved, 2),
         "peak": FP8_PEAK_TFLOPS,
         "unit": "TFLOP/s",

@@ -143,6 +143,20 @@ def _check(status: int, what: str):
         raise MlaError(status, what)
 
 
+def _launch(name: str, args: tuple, keep: tuple, prepare: bool, result):
+    """Call library entry point `name` with the marshalled args and return `result`; with
+    prepare, make no call and return a zero-argument callable that makes exactly this call
+    (same pointers, sizes and stream; `keep` holds the tensors the pointers refer to), so
+    that timing loops measure the launch without the argument checks."""
+    f = getattr(lib(), name)
+    if prepare:
+        def call(_f=f, _args=args, _keep=keep):
+            _check(_f(*_args), name)
+        return call
+    _check(f(*args), name)
+    return result
+
+
 def _stream(stream) -> Optional[int]:
     import torch
 
@@ -239,14 +253,16 @@ def amax_per_head(x, stream=None):
     return amax
 
 
-def quant_static(xs: Sequence, descales: Sequence, outs: Optional[Sequence] = None, stream=None):
+def quant_static(xs: Sequence, descales: Sequence, outs: Optional[Sequence] = None, stream=None,
+                 prepare: bool = False):
     """Quantize 1..3 bf16 tensors [T, H, D] (token/head strides allowed, last dim contiguous)
-    with fp32 [H] descales in ONE launch. Returns uint8 E4M3 code tensors [T, H, D]."""
+    with fp32 [H] descales in ONE launch. Returns uint8 E4M3 code tensors [T, H, D] (with
+    prepare: a callable that repeats the checked launch, see _launch)."""
     if len(xs) != len(descales) or not 1 <= len(xs) <= 3:
         raise ValueError("need 1..3 tensors and one descale vector each")
     jobs, ys, heads = _quant_jobs(xs, descales, outs)
-    _check(lib().mla_fp8_quant_static(jobs, len(xs), heads, _stream(stream)), "mla_fp8_quant_static")
-    return ys
+    return _launch("mla_fp8_quant_static", (jobs, len(xs), heads, _stream(stream)),
+                   (tuple(xs), tuple(descales), tuple(ys)), prepare, ys)
 
 
 def _quant_jobs(xs, descales, outs):
@@ -300,7 +316,7 @@ def quant_dynamic(xs: Sequence, outs: Optional[Sequence] = None, descale_out=Non
 
 
 def kv_produce(c_kv, k_pe, w_kv_b, descale_k, descale_v, out_bf16: bool = False, k8=None,
-               v8=None, stream=None):
+               v8=None, stream=None, prepare: bool = False):
     """Un-absorbed K/V expansion + static quantization. c_kv [T, >=512] and k_pe [T, >=64] bf16
     (row-strided views allowed), w_kv_b bf16 [H*256, 512]. Returns (k8 [T,H,192], v8 [T,H,128]
     uint8 codes) and, with out_bf16, also the bf16 K and V."""
@@ -333,11 +349,12 @@ def kv_produce(c_kv, k_pe, w_kv_b, descale_k, descale_v, out_bf16: bool = False,
     if out_bf16:
         kb = torch.empty((n, heads, D_QK), dtype=torch.bfloat16, device=dev)
         vb = torch.empty((n, heads, D_V), dtype=torch.bfloat16, device=dev)
-    _check(lib().mla_fp8_kv_produce(
+    return _launch("mla_fp8_kv_produce", (
         _ptr(c_kv), c_kv.stride(0), _ptr(k_pe), k_pe.stride(0), _ptr(w_kv_b), n, heads,
         w_kv_b.shape[1], k_pe.shape[1], _ptr(descale_k), _ptr(descale_v), _ptr(k8), _ptr(v8),
-        _ptr(kb), _ptr(vb), _stream(stream)), "mla_fp8_kv_produce")
-    return (k8, v8, kb, vb) if out_bf16 else (k8, v8)
+        _ptr(kb), _ptr(vb), _stream(stream)),
+        (c_kv, k_pe, w_kv_b, descale_k, descale_v, k8, v8, kb, vb), prepare,
+        (k8, v8, kb, vb) if out_bf16 else (k8, v8))
 
 
 def _attention_args(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, lse_stride, descales):
@@ -376,9 +393,11 @@ def _attention_args(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse, lse_st
 
 def prefill_varlen(q8, k8, v8, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                    descale_q, descale_k, descale_v, softmax_scale: float, causal: bool,
-                   out=None, lse=None, lse_stride: Optional[int] = None, stream=None):
+                   out=None, lse=None, lse_stride: Optional[int] = None, stream=None,
+                   prepare: bool = False):
     """FP8 varlen attention. q8 [Tq,H,192], k8 [Tk,H,192], v8 [Tk,H,128] uint8 codes (contiguous);
-    cu_seqlens int32 [B+1] on device. Returns (out bf16 [Tq,H,128], lse fp32 [H, lse_stride])."""
+    cu_seqlens int32 [B+1] on device. Returns (out bf16 [Tq,H,128], lse fp32 [H, lse_stride])
+    (with prepare: a callable that repeats the checked launch, see _launch)."""
     import torch
 
     out, lse, lse_stride = _attention_args(
@@ -386,12 +405,13 @@ def prefill_varlen(q8, k8, v8, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, ma
         {"descale_q": descale_q, "descale_k": descale_k, "descale_v": descale_v})
     tq, heads, tk = q8.shape[0], q8.shape[1], k8.shape[0]
     batch = cu_seqlens_q.shape[0] - 1
-    _check(lib().mla_fp8_prefill_varlen(
+    return _launch("mla_fp8_prefill_varlen", (
         _ptr(q8), _ptr(k8), _ptr(v8), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
         int(max_seqlen_q), int(max_seqlen_k), tq, tk, heads, q8.shape[2], v8.shape[2],
         _ptr(descale_q), _ptr(descale_k), _ptr(descale_v), float(softmax_scale), int(bool(causal)),
-        _ptr(out), _ptr(lse), int(lse_stride), _stream(stream)), "mla_fp8_prefill_varlen")
-    return out, lse
+        _ptr(out), _ptr(lse), int(lse_stride), _stream(stream)),
+        (q8, k8, v8, cu_seqlens_q, cu_seqlens_k, descale_q, descale_k, descale_v, out, lse),
+        prepare, (out, lse))
 
 
 def prefill_varlen_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
@@ -413,8 +433,10 @@ def prefill_varlen_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, 
     return out, lse
 
 
-def merge_lse(outs: Sequence, lses: Sequence, out=None, lse_out=None, stream=None):
-    """Merge partials: outs bf16 [T,H,128] each, lses fp32 [H, ld] each (same ld)."""
+def merge_lse(outs: Sequence, lses: Sequence, out=None, lse_out=None, stream=None,
+              prepare: bool = False):
+    """Merge partials: outs bf16 [T,H,128] each, lses fp32 [H, ld] each (same ld). Returns
+    (out, lse_out) (with prepare: a callable that repeats the checked launch, see _launch)."""
     import torch
 
     n = len(outs)
@@ -445,9 +467,9 @@ def merge_lse(outs: Sequence, lses: Sequence, out=None, lse_out=None, stream=Non
         ld_out = tq
     op = (_c_vp * n)(*[_ptr(o) for o in outs])
     lp = (_c_vp * n)(*[_ptr(l_) for l_ in lses])
-    _check(lib().mla_merge_lse(n, op, lp, ld_in, tq, heads, D_V, _ptr(out), _ptr(lse_out),
-                               ld_out, _stream(stream)), "mla_merge_lse")
-    return out, lse_out
+    return _launch("mla_merge_lse", (n, op, lp, ld_in, tq, heads, D_V, _ptr(out), _ptr(lse_out),
+                                     ld_out, _stream(stream)),
+                   (tuple(outs), tuple(lses), out, lse_out), prepare, (out, lse_out))
 
 
 def chunked_workspace_size(lq: int, lk: int, n_heads: int, seg_len: int, causal: bool = True) -> int:
@@ -489,9 +511,11 @@ def prefill_chunked_noalloc(q8, k8, v8, descale_q, descale_k, descale_v, softmax
 
 
 def prefill_chunked(q8, k8, v8, descale_q, descale_k, descale_v, softmax_scale: float, seg_len: int,
-                    causal: bool = True, out=None, lse=None, workspace=None, stream=None):
+                    causal: bool = True, out=None, lse=None, workspace=None, stream=None,
+                    prepare: bool = False):
     """One sequence of Lq queries (the last Lq of Lk tokens) over context segments of seg_len
-    keys with one quantized Q; partials merged in the library. Returns (out, lse)."""
+    keys with one quantized Q; partials merged in the library. Returns (out, lse) (with
+    prepare: a callable that repeats the checked launch, see _launch)."""
     import torch
 
     _tensor("q8", q8, torch.uint8, (None, None, D_QK))
@@ -518,8 +542,8 @@ def prefill_chunked(q8, k8, v8, descale_q, descale_k, descale_v, softmax_scale: 
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q8.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    _check(lib().mla_fp8_prefill_chunked(
+    return _launch("mla_fp8_prefill_chunked", (
         _ptr(q8), _ptr(k8), _ptr(v8), lq, lk, heads, _ptr(descale_q), _ptr(descale_k),
         _ptr(descale_v), float(softmax_scale), int(seg_len), int(bool(causal)), _ptr(out), _ptr(lse),
-        lse_stride, _ptr(workspace), ws_bytes, _stream(stream)), "mla_fp8_prefill_chunked")
-    return out, lse
+        lse_stride, _ptr(workspace), ws_bytes, _stream(stream)),
+        (q8, k8, v8, descale_q, descale_k, descale_v, out, lse, workspace), prepare, (out, lse))
