@@ -274,13 +274,23 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   void* out_ptr = p.out;
   float* lse_ptr = p.lse;
   if constexpr (kNSeg > 1) {
-    // multi-segment launch: segments in the host's order (heaviest first), then query
-    // tiles from the last, heads fastest
-    int idx = blockIdx.x;
-    h = idx % H;
-    idx /= H;
-    m_tile = p.n_m_tiles - 1 - idx % p.n_m_tiles;
-    const int e = idx / p.n_m_tiles;
+    // multi-segment launch: segments in the host's order (heaviest first); within a
+    // segment the XCD-aware order of the single-sequence launch below (its block range
+    // starts at a multiple of 8, so block % 8 is still the XCD), else query tiles from the
+    // last, heads fastest
+    const int per_seg = p.n_m_tiles * H;
+    const int e = blockIdx.x / per_seg;
+    const int local = blockIdx.x - e * per_seg;
+    if (p.xcd_order) {
+      const int hp = H >> 2;
+      const int slot = local >> 3;
+      const int half = hp * (local & 7) + slot % hp;
+      h = half >> 1;
+      m_tile = p.n_m_tiles - 2 + (half & 1) - 2 * (slot / hp);
+    } else {
+      h = local % H;
+      m_tile = p.n_m_tiles - 1 - local / H;
+    }
     const SegDev& sg = st.e[e];
     k0 = min(max(sg.k0, (int64_t)0), p.total_k);
     k1 = min(k0 + sg.lk, p.total_k);
@@ -1004,6 +1014,9 @@ int prefill_launch_segments(const PrefillArgs& a, const PrefillSegment* segs, in
   }
   const int64_t blocks = n_m * n * a.n_heads;
   if (blocks >= (1ll << 31)) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
+  // XCD-aware order within each segment (measured: the 16,384-row chunks of a
+  // 131,072-token context 1.1-1.3 % faster, 4,096-row chunks unchanged)
+  prm.xcd_order = (a.n_heads % 4 == 0 && n_m % 2 == 0) ? 1 : 0;
   hipLaunchKernelGGL((prefill_fp8_kernel<kMaxPrefillSegments, kPvMode>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kThreads), 0, stream, prm, tab);
   return check_launch("prefill_fp8_kernel");
