@@ -134,3 +134,21 @@ def test_kv_produce_rejects():
         B.kv_produce(c[:, :512], c[:, 512:], w, _f32(H), _f32(H), k8=_u8(TK, H, 128))
     with pytest.raises(ValueError, match="must be a CUDA tensor"):
         B.kv_produce(c[:, :512], c[:, 512:], w, _f32(H), _f32(H))
+
+
+def test_prepare_checks_like_the_call():
+    """prepare=True runs the same checks before it returns a callable, so a bad argument
+    raises at preparation, never at a later launch."""
+    with pytest.raises(ValueError, match="q must have shape"):
+        _prefill(q8=_u8(TQ, H, 128), prepare=True)
+    with pytest.raises(ValueError, match="must be a CUDA tensor"):
+        _prefill(prepare=True)
+    with pytest.raises(ValueError, match="v8 must have shape"):
+        _chunked(v8=_u8(TK - 1, H, 128), prepare=True)
+    with pytest.raises(ValueError, match="out\\[0\\] must have shape"):
+        B.quant_static([_bf(TQ, H, 192)], [_f32(H)], outs=[_u8(TQ, H, 128)], prepare=True)
+    with pytest.raises(ValueError, match="must be a CUDA tensor"):
+        B.merge_lse([_bf(TQ, H, 128)], [_f32(H, TQ)], prepare=True)
+    c = _bf(TK, 576)
+    with pytest.raises(ValueError, match="descale_k must have shape"):
+        B.kv_produce(c[:, :512], c[:, 512:], _bf(H * 256, 512), _f32(H + 1), _f32(H), prepare=True)
