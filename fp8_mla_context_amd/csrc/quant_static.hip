@@ -31,9 +31,7 @@ struct QuantJobDev {
   int64_t stride_token;
   int64_t stride_head;
   int64_t n_tokens;
-  uint32_t chunk_begin;  // first global chunk index of this job (amax kernel)
-  uint32_t n_chunks;
-  uint32_t block_begin;  // first workgroup of this job (quantizer)
+  uint32_t block_begin;  // first workgroup of this job
   int32_t head_dim;
   int32_t vec;        // 1: 16-byte loads are aligned
   int32_t from_amax;  // 1: descale = descale_of_amax(descale[h])
@@ -42,7 +40,6 @@ struct QuantJobDev {
 struct QuantParams {
   QuantJobDev job[kMaxJobs];
   int32_t n_jobs;
-  uint32_t total_chunks;
   uint32_t total_blocks;
   mla::FastDiv heads;
 };
@@ -54,6 +51,29 @@ constexpr int kTileTokens = 256;  // tokens of one (tensor, head) per quantizer 
 __device__ __forceinline__ float descale_of_amax(float amax) {
   if (!(amax > 0.f)) return 1.f;
   return fmaxf(__fdiv_rn(amax, 448.f), 0x1p-126f);
+}
+
+// Chunk c (16 consecutive elements) of a token tile whose (token 0, head) row starts at
+// src0: its inputs in w, elements 2i and 2i+1 in w[i]. Returns the chunk's token in the tile
+// (chunks of a row: 12 for head dim 192, else 8) and its column in *col.
+__device__ __forceinline__ int load_tile_chunk(const QuantJobDev& jb, const uint16_t* src0,
+                                               bool wide, int c, uint32_t (&w)[8],
+                                               int* col = nullptr) {
+  const int t = wide ? c / 12 : c >> 3;
+  const int cc = c - t * (wide ? 12 : 8);
+  if (col != nullptr) *col = cc;
+  const uint16_t* src = src0 + t * jb.stride_token + cc * 16;
+  if (jb.vec) {
+    const uint4 a = *reinterpret_cast<const uint4*>(src);
+    const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = static_cast<uint32_t>(src[2 * i]) | (static_cast<uint32_t>(src[2 * i + 1]) << 16);
+  }
+  return t;
 }
 
 // Workgroup b: its job (blocks [job.block_begin, next job's)), then token tile and head,
@@ -86,19 +106,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_static_kernel(QuantParams
   const int64_t dst_rs = static_cast<int64_t>(p.heads.d) * jb.head_dim;
   // chunk c of the tile: its 16 inputs in w (elements 2i, 2i+1 in w[i]), its codes' address
   auto load = [&](int c, uint32_t (&w)[8]) {
-    const int t = wide ? c / 12 : c >> 3;
-    const int col = c - t * (wide ? 12 : 8);
-    const uint16_t* src = src0 + t * jb.stride_token + col * 16;
-    if (jb.vec) {
-      const uint4 a = *reinterpret_cast<const uint4*>(src);
-      const uint4 bb = *reinterpret_cast<const uint4*>(src + 8);
-      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-      w[4] = bb.x; w[5] = bb.y; w[6] = bb.z; w[7] = bb.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        w[i] = static_cast<uint32_t>(src[2 * i]) | (static_cast<uint32_t>(src[2 * i + 1]) << 16);
-    }
+    int col;
+    const int t = load_tile_chunk(jb, src0, wide, c, w, &col);
     return dst0 + t * dst_rs + col * 16;
   };
   auto codes = [&](const uint32_t (&w)[8]) {
@@ -134,78 +143,52 @@ __global__ __launch_bounds__(kQuantThreads) void zero_words_kernel(uint32_t* p, 
   if (i < n) p[i] = 0u;
 }
 
-constexpr int kAmaxLdsSlots = 3 * 1024;  // n_jobs * n_heads maxima kept in LDS
-
 // amax_bits[j * H + h] receives the max of job j, head h (the jobs' descale field is
-// not read)
+// not read). Workgroup b covers the (job, token tile, head) of the quantizer's workgroup
+// b: a running max per thread, a reduction over the workgroup, one global atomic.
 __global__ __launch_bounds__(kQuantThreads) void amax_chunks_kernel(QuantParams p,
                                                                     uint32_t* amax_bits) {
-  __shared__ uint32_t smax[kAmaxLdsSlots];
-  const int H = static_cast<int>(p.heads.d);
-  const int slots = p.n_jobs * H;
-  const bool use_lds = slots <= kAmaxLdsSlots;
-  if (use_lds)
-    for (int i = threadIdx.x; i < slots; i += kQuantThreads) smax[i] = 0u;
-  __syncthreads();
-  const uint32_t stride = gridDim.x * kQuantThreads;
-  for (uint32_t c = blockIdx.x * kQuantThreads + threadIdx.x; c < p.total_chunks; c += stride) {
-    int j = 0;
-    if (p.n_jobs > 1 && c >= p.job[1].chunk_begin) j = 1;
-    if (p.n_jobs > 2 && c >= p.job[2].chunk_begin) j = 2;
-    const QuantJobDev& jb = p.job[j];
-    const uint32_t local = c - jb.chunk_begin;
-    uint32_t row, col;
-    if (jb.head_dim == 192) {
-      row = local / 12u;
-      col = local - row * 12u;
-    } else {
-      row = local >> 3;
-      col = local & 7u;
-    }
-    const uint32_t t = mla::fdiv(row, p.heads);
-    const uint32_t h = row - t * p.heads.d;
-    const uint16_t* src = jb.x + static_cast<int64_t>(t) * jb.stride_token +
-                          static_cast<int64_t>(h) * jb.stride_head + col * 16u;
+  __shared__ uint32_t wave_max[kQuantThreads / 64];
+  const uint32_t b = blockIdx.x;
+  int j = 0;
+  if (p.n_jobs > 1 && b >= p.job[1].block_begin) j = 1;
+  if (p.n_jobs > 2 && b >= p.job[2].block_begin) j = 2;
+  const QuantJobDev& jb = p.job[j];
+  const uint32_t local = b - jb.block_begin;
+  const uint32_t tile = mla::fdiv(local, p.heads);
+  const uint32_t h = local - tile * p.heads.d;
+  const int64_t t0 = static_cast<int64_t>(tile) * kTileTokens;
+  const int n_tok = static_cast<int>(min<int64_t>(kTileTokens, jb.n_tokens - t0));
+  const bool wide = jb.head_dim == 192;
+  const int n_chunks = n_tok * (wide ? 12 : 8);
+  const uint16_t* src0 = jb.x + t0 * jb.stride_token + static_cast<int64_t>(h) * jb.stride_head;
+  auto chunk_max = [&](int c) {
     uint32_t w[8];
-    if (jb.vec) {
-      const uint4 a = *reinterpret_cast<const uint4*>(src);
-      const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
-      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-      w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        w[i] = static_cast<uint32_t>(src[2 * i]) | (static_cast<uint32_t>(src[2 * i + 1]) << 16);
-    }
+    load_tile_chunk(jb, src0, wide, c, w);
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-    const int slot = j * H + static_cast<int>(h);
-    if (use_lds)
-      atomicMax(smax + slot, m << 16);
-    else
-      atomicMax(amax_bits + slot, m << 16);
-  }
+    return m;
+  };
+  uint32_t m = 0;
+  int c = threadIdx.x;
+  for (; c + kQuantThreads < n_chunks; c += 2 * kQuantThreads)
+    m = max(m, max(chunk_max(c), chunk_max(c + kQuantThreads)));
+  if (c < n_chunks) m = max(m, chunk_max(c));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (use_lds)
-    for (int i = threadIdx.x; i < slots; i += kQuantThreads)
-      if (smax[i] != 0u) atomicMax(amax_bits + i, smax[i]);
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kQuantThreads / 64; ++w) m = max(m, wave_max[w]);
+    if (m != 0u) atomicMax(amax_bits + j * static_cast<int>(p.heads.d) + h, m << 16);
+  }
 }
 
 // in place: amax bit patterns -> dynamic descales
 __global__ __launch_bounds__(kQuantThreads) void descale_of_amax_kernel(float* v, int n) {
   int i = blockIdx.x * kQuantThreads + threadIdx.x;
   if (i < n) v[i] = descale_of_amax(v[i]);
-}
-
-// Grid of a grid-stride launch: at most blocks_per_cu blocks of 256 threads per CU (256
-// CUs). The amax reduction takes 16 (one global atomic per head and workgroup).
-int grid_for(uint64_t work_items, int per_block, int blocks_per_cu) {
-  uint64_t blocks = (work_items + per_block - 1) / per_block;
-  const uint64_t cap = 256ull * static_cast<uint64_t>(blocks_per_cu);
-  if (blocks > cap) blocks = cap;
-  if (blocks < 1) blocks = 1;
-  return static_cast<int>(blocks);
 }
 
 // Validate the jobs and fill the launch parameters. need_y: the job writes codes;
@@ -246,8 +229,6 @@ int build_params(const mla_quant_job* jobs, int32_t n_jobs, int32_t n_heads, boo
     d.stride_head = s.stride_head;
     d.head_dim = s.head_dim;
     d.n_tokens = s.n_tokens;
-    d.chunk_begin = static_cast<uint32_t>(total);
-    d.n_chunks = static_cast<uint32_t>(chunks);
     d.block_begin = static_cast<uint32_t>(blocks);
     blocks += static_cast<uint64_t>((s.n_tokens + kTileTokens - 1) / kTileTokens) *
               static_cast<uint64_t>(n_heads);
@@ -259,7 +240,6 @@ int build_params(const mla_quant_job* jobs, int32_t n_jobs, int32_t n_heads, boo
     if (total >= (1ull << 31))
       return mla::fail(MLA_ERR_UNSUPPORTED, "more than 2^35 elements in one launch");
   }
-  p.total_chunks = static_cast<uint32_t>(total);
   p.total_blocks = static_cast<uint32_t>(blocks);
   p.heads = mla::make_fastdiv(static_cast<uint32_t>(n_heads));
   return MLA_OK;
@@ -271,8 +251,8 @@ int launch_amax(const QuantParams& p, uint64_t total, uint32_t* amax_bits, int n
                      dim3(kQuantThreads), 0, st, amax_bits, n);
   int s = mla::check_launch("zero_words_kernel");
   if (s != MLA_OK || total == 0) return s;
-  hipLaunchKernelGGL(amax_chunks_kernel, dim3(grid_for(total, kQuantThreads, 16)),
-                     dim3(kQuantThreads), 0, st, p, amax_bits);
+  hipLaunchKernelGGL(amax_chunks_kernel, dim3(p.total_blocks), dim3(kQuantThreads), 0, st, p,
+                     amax_bits);
   return mla::check_launch("amax_chunks_kernel");
 }
 
