@@ -127,12 +127,14 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_bf16_kernel(Bf16Pa
     h = half >> 1;
     m_tile = p.n_m_tiles - 2 + (half & 1) - 2 * rank;
   } else {
-    int idx = blockIdx.x;
-    h = idx % H;
-    idx /= H;
-    b = idx % p.batch;
-    idx /= p.batch;
-    m_tile = p.n_m_tiles - 1 - idx;
+    // heaviest query tiles first; (sequence, head) pairs rotated by 3 per tile index so
+    // that each XCD (block % 8) sees every pair (the FP8 kernel's varlen order)
+    const int pairs = H * p.batch;
+    const int mi = blockIdx.x / pairs;
+    const int pr = (blockIdx.x - mi * pairs + 3 * mi) % pairs;
+    h = pr % H;
+    b = pr / H;
+    m_tile = p.n_m_tiles - 1 - mi;
   }
 
   int64_t q0 = p.cu_q[b], q1 = p.cu_q[b + 1], k0 = p.cu_k[b], k1 = p.cu_k[b + 1];

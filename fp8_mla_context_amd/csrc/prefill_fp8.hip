@@ -311,13 +311,17 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
     h = half >> 1;
     m_tile = p.n_m_tiles - 2 + (half & 1) - 2 * rank;
   } else {
-    // heaviest query tiles first; heads, then sequences, vary fastest
-    int idx = blockIdx.x;
-    h = idx % H;
-    idx /= H;
-    b = idx % p.batch;
-    idx /= p.batch;
-    m_tile = p.n_m_tiles - 1 - idx;
+    // heaviest query tiles first; within a tile index, the (sequence, head) pairs with
+    // heads fastest, rotated by 3 per tile index: blocks go to XCD block % 8, and with a
+    // multiple of 8 pairs per tile index an unrotated order would give each XCD the same
+    // pairs at every tile index (sequences of unequal length: unequal XCD loads; measured
+    // on 8 packed sequences of 808-3946 tokens, 6 % faster rotated)
+    const int pairs = H * p.batch;
+    const int mi = blockIdx.x / pairs;
+    const int pr = (blockIdx.x - mi * pairs + 3 * mi) % pairs;
+    h = pr % H;
+    b = pr / H;
+    m_tile = p.n_m_tiles - 1 - mi;
   }
 
   // packed sequences from cu_seqlens, or one sequence spanning all tokens
