@@ -96,9 +96,9 @@ def test_zero_tokens_is_noop(gpu_lib):
 
 
 def test_many_heads_scale_lookup_without_lds_table(gpu_lib):
-    """More (tensor, head) slots (3 x 1100) than the quantizer's descale table and the amax
-    kernel's maxima hold in LDS: both then read and update memory per chunk; codes and
-    descales stay bit-exact, for the static and the dynamic path."""
+    """Many (tensor, head) pairs (3 x 1100) of a few tokens each: one workgroup, one code
+    table and one amax reduction per pair; codes and descales stay bit-exact, for the
+    static and the dynamic path."""
     B = gpu_lib
     rng = np.random.default_rng(7)
     T, H = 5, 1100
@@ -115,3 +115,38 @@ def test_many_heads_scale_lookup_without_lds_table(gpu_lib):
         c_ref, d_ref = oracle.quant_dynamic(x)
         assert np.array_equal(host(d_gpu[i]), d_ref)
         assert np.array_equal(host(g), c_ref)
+
+
+def test_descales_at_the_contract_edges(gpu_lib):
+    """Every bf16 pattern at descales 2^-126 and 2^126 and next to them: the code table's
+    window then starts below binade 0 or ends above binade 255 (entries that no bf16
+    magnitude reaches); codes stay those of the exact quotient."""
+    B = gpu_lib
+    desc = np.array([2.0 ** -126, 1.5 * 2.0 ** -126, 1.999 * 2.0 ** -120, 2.0 ** 126,
+                     1.75 * 2.0 ** 125, 2.0 ** 120], dtype=np.float32)
+    x = _exhaustive_tensor(desc.shape[0], 128)
+    (y,) = B.quant_static([dev_bf16(x)], [dev(desc)])
+    got = host(y)
+    exp = oracle.quant_static(x, desc)
+    bad = np.argwhere(got != exp)
+    assert bad.size == 0, [(tuple(i), hex(int(x[tuple(i)])), int(got[tuple(i)]), int(exp[tuple(i)]))
+                           for i in bad[:8]]
+
+
+def test_jobs_of_different_lengths_with_an_empty_one(gpu_lib):
+    """Three jobs in one launch, the middle one empty: each job's workgroups cover exactly
+    its own tokens (257, 0 and 700 tokens; ragged last tiles)."""
+    B = gpu_lib
+    rng = np.random.default_rng(11)
+    H = 12
+    shapes = [(257, H, 192), (0, H, 192), (700, H, 128)]
+    xs, ds = [], []
+    for shp in shapes:
+        z = (rng.standard_normal(shp) * 3).astype(np.float32)
+        xs.append(((z.view(np.uint32) + 0x8000) >> 16).astype(np.uint16))
+        ds.append(np.exp2(rng.uniform(-8, 0, H)).astype(np.float32))
+    got = B.quant_static([dev_bf16(x) for x in xs], [dev(d) for d in ds])
+    for g, x, d in zip(got, xs, ds):
+        assert tuple(g.shape) == x.shape
+        if x.shape[0]:
+            assert np.array_equal(host(g), oracle.quant_static(x, d))
