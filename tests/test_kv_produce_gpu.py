@@ -116,3 +116,19 @@ def test_kv_produce_32k_sampled(gpu_lib):
     n = 32768
     rows = np.unique(np.concatenate([[0, 1, 127, 128, n - 129, n - 1], rng.integers(0, n, 250)]))
     _check(gpu_lib, n, 12, 9, sample=rows)
+
+
+def test_kv_produce_descales_across_the_contract(gpu_lib):
+    """One descale per head across the contract [2^-126, 2^126]: its edges (where the code
+    table's window starts below binade 0 or ends above binade 255), scales that put most
+    codes among the E4M3 subnormals (64) or saturate them (2^-6), and ordinary ones. Every
+    code equals the oracle quantizer's on the kernel's own bf16 value."""
+    B = gpu_lib
+    heads = 12
+    cache, w = make_latent(21, 300, heads)
+    d = np.array([2.0 ** -126, 2.0 ** 126, 64.0, 2.0 ** -6, 1.0, 0.0123, 3.0, 1.0 / 448,
+                  2.0 ** -120, 2.0 ** 120, 0.7, 5.0], dtype=np.float32)
+    dk, dv = d, d[::-1].copy()
+    k8, v8, kb, vb = _run(B, cache, w, dk, dv, out_bf16=True)
+    assert np.array_equal(k8, oracle.quant_static(kb, dk))
+    assert np.array_equal(v8, oracle.quant_static(vb, dv))
