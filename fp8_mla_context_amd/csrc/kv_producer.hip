@@ -12,18 +12,20 @@
 // W is [H * 256, 512] bf16: rows 256 h .. 256 h + 127 are W_UK[h], the next 128 W_UV[h].
 //
 // Design:
-//  * One workgroup = 8 waves = 128 tokens x one head's 256 output features. Y^T = W_h C^T
-//    on v_mfma_f32_32x32x16_bf16 with weight rows as the A operand and latent rows as
-//    the B operand, so a lane's accumulator holds one token and 4 x 4 consecutive
-//    features. Wave w owns tokens 64 (w & 1) .. + 63 and features 64 (w >> 1) .. + 63.
-//    Work items (token tile, head) are dealt to the XCDs in contiguous ranges, so the
-//    twelve workgroups of a token tile share its latent rows in one L2 and the 3 MB
-//    weight stays resident in each XCD's L2.
-//  * The 512-deep reduction runs in 16 chunks of 32; chunk c's weight rows (256 x 64 B)
-//    and latent rows (128 x 64 B) are DMA'd (global_load_lds_dwordx4) into LDS buffer
-//    c % 3, two chunks ahead of their use, the four 16-byte pieces of a row XOR-swizzled
-//    so that the operand reads of 16 consecutive rows hit distinct banks. Two workgroups
-//    share a CU.
+//  * One workgroup = 16 waves = 256 tokens x one head's 256 output features, one per CU.
+//    Y^T = W_h C^T on v_mfma_f32_32x32x16_bf16 with weight rows as the A operand and
+//    latent rows as the B operand, so a lane's accumulator holds one token and 4 x 4
+//    consecutive features. Wave w owns tokens 64 (w & 3) .. + 63 and features
+//    64 (w >> 2) .. + 63. Work items (token tile, head) are dealt to the XCDs in
+//    contiguous ranges, so the twelve workgroups of a token tile share its latent rows in
+//    one L2 and the 3 MB weight stays resident in each XCD's L2.
+//  * The 512-deep reduction runs in 8 chunks of 64; chunk c's weight rows (256 x 128 B)
+//    and latent rows (256 x 128 B) are DMA'd (global_load_lds_dwordx4) into LDS buffer
+//    c % 2, one chunk ahead of their use, the eight 16-byte pieces of a row XOR-swizzled
+//    so that the operand reads of 16 consecutive rows hit distinct banks. Each wave runs
+//    16 MFMAs between two barriers. (Measured against 16 chunks of 32 with two 8-wave
+//    workgroups of 128 tokens per CU and three buffers: 140 against 156 us for 32K
+//    tokens; the 64-byte chunks gave 8 MFMAs per barrier and a burst of loads after each.)
 //  * Epilogue: fp32 -> bf16 (v_cvt_pk_bf16_f32, nearest even) -> E4M3 code, looked up in
 //    per-head tables of the exact quantizer's codes, filled in LDS during the first
 //    chunks of the reduction. The codes pass through LDS so that each thread stores
@@ -51,25 +53,26 @@ constexpr int kRope = 64;
 constexpr int kNope = 128;
 constexpr int kDv = 128;
 constexpr int kFeat = kNope + kDv;  // 256 output features per head
-constexpr int kThreads = 512;       // 8 waves
-constexpr int kTM = 128;            // tokens per workgroup
-constexpr int kKC = 32;             // reduction chunk
+constexpr int kWaves = 16;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTM = 256;            // tokens per workgroup
+constexpr int kKC = 64;             // reduction chunk
 constexpr int kNChunks = kLatent / kKC;
-constexpr int kRowBytes = 64;       // one chunk of a row: four 16-byte pieces, swizzled
-constexpr int kWRegion = kFeat * kRowBytes;  // 16384
-constexpr int kCRegion = kTM * kRowBytes;    // 8192
-constexpr int kStage = kWRegion + kCRegion;  // 24576
-// Three LDS buffers (72 KB, chunks loaded two ahead) leave room for two workgroups per
-// CU, so that one workgroup's quantizing epilogue overlaps the other's projection.
-constexpr int kStages = 3;
-constexpr int kWgPerCu = 2;
-constexpr int kWInstr = kFeat * 4 / 64;  // 16 DMA instructions (4 pieces per row)
-constexpr int kCInstr = kTM * 4 / 64;    // 8
+constexpr int kRowBytes = 128;      // one chunk of a row: eight 16-byte pieces, swizzled
+constexpr int kWRegion = kFeat * kRowBytes;  // 32768
+constexpr int kCRegion = kTM * kRowBytes;    // 32768
+constexpr int kStage = kWRegion + kCRegion;  // 65536
+// Two LDS buffers (128 KB) and the code tables: one workgroup per CU.
+constexpr int kStages = 2;
+constexpr int kWgPerCu = 1;
+constexpr int kWInstr = kFeat * 8 / 64;  // 32 DMA instructions (8 pieces per row)
+constexpr int kCInstr = kTM * 8 / 64;    // 32
 constexpr int kInstr = kWInstr + kCInstr;
-constexpr int kPerWave = (kInstr + 7) / 8;  // 3
-// piece p of row r sits at position p ^ ((r >> 2) & 3): the 16-byte operand reads of 16
-// consecutive rows (same piece) then cover all 64 banks
-__device__ __forceinline__ int piece_pos(int row, int piece) { return piece ^ ((row >> 2) & 3); }
+constexpr int kPerWave = (kInstr + kWaves - 1) / kWaves;  // 4
+// piece p of row r sits at position p ^ ((r >> 1) & 7): the 16-byte operand reads of 16
+// consecutive rows (same piece; 128-byte rows, two rows per 256 bytes of banks) then
+// cover all 64 banks
+__device__ __forceinline__ int piece_pos(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 constexpr int kCodeStride = kFeat + 16;  // LDS bytes per token row of the code tile
 static_assert(kStages * kStage >= kTM * kCodeStride, "the code tile reuses the stage buffers");
 
@@ -113,19 +116,19 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
   const int64_t t0 = static_cast<int64_t>(v / H) * kTM;
   const int n_tok = static_cast<int>(min<int64_t>(kTM, p.n_tokens - t0));  // >= 1
 
-  // DMA slots: instruction i (i = wave + 8 j) writes 16-byte LDS slots 64 i + lane of the
-  // stage; slots 0..1023 are weight rows (4 per row), then 512 slots of latent rows (rows
-  // past the last token repeat it). Slot position q of row r holds piece q ^ ((r >> 2) & 3).
+  // DMA slots: instruction i (i = wave + 16 j) writes 16-byte LDS slots 64 i + lane of the
+  // stage; slots 0..2047 are weight rows (8 per row), then 2048 slots of latent rows (rows
+  // past the last token repeat it). Slot position q of row r holds piece q ^ ((r >> 1) & 7).
   const uint8_t* w_base = reinterpret_cast<const uint8_t*>(p.w) +
                           static_cast<int64_t>(h) * kFeat * kLatent * 2;
   const uint8_t* c_base = reinterpret_cast<const uint8_t*>(p.c_kv) + t0 * p.c_stride * 2;
   uint32_t dma_off[kPerWave];
 #pragma unroll
   for (int j = 0; j < kPerWave; ++j) {
-    const int i = min(wave + 8 * j, kInstr - 1);
+    const int i = min(wave + kWaves * j, kInstr - 1);
     const int s = (i < kWInstr ? i * 64 : (i - kWInstr) * 64) + lane;
-    const int row = s >> 2;
-    const int piece = piece_pos(row, s & 3);  // the swizzle is its own inverse
+    const int row = s >> 3;
+    const int piece = piece_pos(row, s & 7);  // the swizzle is its own inverse
     if (i < kWInstr)
       dma_off[j] = static_cast<uint32_t>(row * kLatent * 2 + 16 * piece);
     else
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
     uint8_t* stage = lds + (c % kStages) * kStage;
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
-      const int i = wave + 8 * j;  // wave-uniform
+      const int i = wave + kWaves * j;  // wave-uniform
       if (i < kInstr) {
         const uint8_t* base = uniform_ptr((i < kWInstr ? w_base : c_base) + c * kKC * 2);
         const uint32_t dst =
@@ -144,10 +147,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
       }
     }
   };
-  const int n_mine = (kInstr - wave + 7) / 8;  // DMA instructions of this wave per chunk
+  const int n_mine = (kInstr - wave + kWaves - 1) / kWaves;  // DMA instructions of this wave per chunk
 
   const int g = lane >> 5, col = lane & 31;
-  const int tq = wave & 1, fq = wave >> 1;
+  const int tq = wave & 3, fq = wave >> 2;
   v16f acc[2][2];
 #pragma unroll
   for (int fb = 0; fb < 2; ++fb)
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
     if (next < kNChunks) issue(next++);
     const uint8_t* stage = lds + (c % kStages) * kStage;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < kKC / 16; ++ks) {
       v8bf a[2], b[2];
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb) {
