@@ -16,9 +16,9 @@
 //    Y^T = W_h C^T on v_mfma_f32_32x32x16_bf16 with weight rows as the A operand and
 //    latent rows as the B operand, so a lane's accumulator holds one token and 4 x 4
 //    consecutive features. Wave w owns tokens 64 (w & 3) .. + 63 and features
-//    64 (w >> 2) .. + 63. Work items (token tile, head) are dealt to the XCDs in
-//    contiguous ranges, so the twelve workgroups of a token tile share its latent rows in
-//    one L2 and the 3 MB weight stays resident in each XCD's L2.
+//    64 (w >> 2) .. + 63. Each XCD takes half of the heads over a quarter of the token
+//    tiles, so that its L2 holds those heads' weights and serves each token tile's
+//    latent rows to them.
 //  * The 512-deep reduction runs in 8 chunks of 64; chunk c's weight rows (256 x 128 B)
 //    and latent rows (256 x 128 B) are DMA'd (global_load_lds_dwordx4) into LDS buffer
 //    c % 2, one chunk ahead of their use, the eight 16-byte pieces of a row XOR-swizzled
@@ -92,7 +92,7 @@ struct ProducerParams {
   int64_t pe_stride;  // elements between rope rows
   int64_t n_tokens;
   int32_t n_heads;
-  int32_t xcd_order;  // 1: the grid size is a multiple of 8 (see the block mapping)
+  int32_t xcd_order;  // 2 or 1: XCD-aware work item orders (see the block mapping)
 };
 
 __device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v16f& c) {
@@ -106,14 +106,26 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void kv_producer_kernel(Produce
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = p.n_heads;
-  // Work item v = (tile, head), heads fastest. With xcd_order, workgroup b (dealt to XCD
-  // b % 8) takes v = (b % 8) * (blocks / 8) + b / 8: each XCD gets a contiguous range, so
-  // the twelve heads of a token tile read its latent rows through one L2, and W stays
-  // resident there.
+  // Work items (token tile, head); workgroup b is dealt to XCD b % 8. With xcd_order 2
+  // (H even, tile count a multiple of 4) XCD x takes half of the heads (x & 1) over a
+  // quarter of the token tiles (x >> 1), heads fastest: its L2 then holds the weights of
+  // H/2 heads (1.5 MB at 12 heads, against 4 MB of L2) and serves a token tile's latent
+  // rows to those heads, each latent row being read by two XCDs. (All H heads of a
+  // contiguous range per XCD, xcd_order 1, left the 3 MB of weights competing with the
+  // latent rows: 120 MB fetched from HBM on 32K tokens against 94 MB, and 3 % slower.)
+  // Otherwise v = blockIdx is (tile, head), heads fastest.
   const int nb = gridDim.x;
-  const int v = p.xcd_order ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  const int h = v % H;
-  const int64_t t0 = static_cast<int64_t>(v / H) * kTM;
+  int h, tile;
+  if (p.xcd_order == 2) {
+    const int x = blockIdx.x & 7, s = blockIdx.x >> 3, hh = H >> 1;
+    tile = (x >> 1) * (nb / (4 * H)) + s / hh;
+    h = hh * (x & 1) + s % hh;
+  } else {
+    const int v = p.xcd_order ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+    h = v % H;
+    tile = v / H;
+  }
+  const int64_t t0 = static_cast<int64_t>(tile) * kTM;
   const int n_tok = static_cast<int>(min<int64_t>(kTM, p.n_tokens - t0));  // >= 1
 
   // DMA slots: instruction i (i = wave + 16 j) writes 16-byte LDS slots 64 i + lane of the
@@ -332,7 +344,7 @@ extern "C" int mla_fp8_kv_produce(const void* c_kv, int64_t c_kv_stride, const v
   prm.pe_stride = k_pe_stride;
   prm.n_tokens = n_tokens;
   prm.n_heads = n_heads;
-  prm.xcd_order = (tiles * n_heads) % 8 == 0 ? 1 : 0;
+  prm.xcd_order = (n_heads % 2 == 0 && tiles % 4 == 0) ? 2 : ((tiles * n_heads) % 8 == 0 ? 1 : 0);
   hipLaunchKernelGGL(kv_producer_kernel, dim3(static_cast<unsigned>(tiles * n_heads)),
                      dim3(kThreads), 0, static_cast<hipStream_t>(stream), prm);
   return mla::check_launch("kv_producer_kernel");
