@@ -16,15 +16,17 @@ __device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
 
 // global_load_lds_dwordx4 from base + off (base wave-uniform, off per lane) to LDS
 // address lds_addr + 16 * lane. Issued as inline assembly so that the compiler does not
-// wait for it before unrelated LDS reads; completion is tracked with wait_vmcnt.
+// wait for it before unrelated LDS reads; completion is tracked with wait_vmcnt. The LDS
+// address goes in through an m0 operand, so the compiler writes m0 itself and knows it
+// (m0 cannot be declared clobbered); the nop is the wait state between that write and
+// the DMA.
 __device__ __forceinline__ void dma_load16(const uint8_t* base, uint32_t off, uint32_t lds_addr) {
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(off), "s"(base), "s"(lds_addr)
-      : "memory", "m0");
+      : "v"(off), "s"(base), "{m0}"(lds_addr)
+      : "memory");
 }
 
 // wait until at most n (wave-uniform, 0..15) vector-memory loads of this wave are outstanding

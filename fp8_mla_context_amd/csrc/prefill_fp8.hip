@@ -16,10 +16,10 @@
 //  * 64-key K tiles and FP8 V tiles live in two LDS buffers each, filled by
 //    global->LDS DMA (global_load_lds_dwordx4, no register staging). K rows are padded to
 //    208 bytes; V rows are 128 bytes with XOR-swizzled 16-byte chunks (see v_swizzle).
-//    Iteration t issues the loads of K(t+2) and V(t+1) at its start, then the S MFMAs of
-//    tile t+1 with the row max of tile t and the conversion of V tile t to bf16 V^T (two
-//    V^T buffers) between them, then the PV MFMAs of tile t-1 with the exponentials of
-//    tile t between them (exponentials co-issue with bf16 MFMAs, hardly with FP8 ones);
+//    Iteration t issues the S MFMAs of tile t+1 with the row max of tile t and the
+//    conversion of V tile t to bf16 V^T (two V^T buffers) between them, then the loads of
+//    K(t+2) and V(t+1), then the PV MFMAs of tile t-1 with the exponentials of tile t
+//    between them (exponentials co-issue with bf16 MFMAs, hardly with FP8 ones);
 //    one barrier per tile.
 //  * S^T = K * Q^T on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3 -> fp32): the Q fragment
 //    (32 rows x 192) stays in registers as the B operand, K rows are read from LDS as
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   //
   // Schedule: K, V and V^T of tile t live in buffer t % 2 of their kind. Iteration t
   // reads K(t+1) (S of the next tile), V(t) (converted to V^T) and the V^T of tile t-1
-  // (PV of the previous tile), and issues K(t+2) and V(t+1) at its start, into the
+  // (PV of the previous tile), and issues K(t+2) and V(t+1) after its S MFMAs, into the
   // buffers that K(t) and V(t-1) left at the previous barrier; they land before the
   // iteration's closing barrier.
   constexpr int kKInstr = kBN * (kKStride / 16) / 64;  // 13
@@ -545,11 +545,11 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
   };
   // One software-pipelined iteration. S of tile it is in s_c, the bf16 P of tile it-1 in
   // pb_p and its V^T in V^T buffer (it-1) % 2 (on iteration 0: zero P and a zeroed
-  // buffer). The iteration loads K(it+2) and V(it+1) into the buffers that K(it) and
-  // V(it-1) left at the previous barrier. It first issues the 6 S MFMAs of tile it+1 with
-  // the VALU work that needs no exponentials spread between them (mask and row max of S
-  // block 0; row max of block 1; rescale test; transposed reads of V tile it; their
-  // conversion to V^T buffer it % 2), then the 16 PV MFMAs of tile it-1 with
+  // buffer). It first issues the 6 S MFMAs of tile it+1 with the VALU work that needs no
+  // exponentials spread between them (mask and row max of S block 0; row max of block 1;
+  // rescale test; transposed reads of V tile it; their conversion to V^T buffer it % 2),
+  // then the loads of K(it+2) and V(it+1) into the buffers that K(it) and V(it-1) left at
+  // the previous barrier, then the 16 PV MFMAs of tile it-1 with
   // one softmax pair of tile it (P to pb_c) after each: exponentials overlap bf16 MFMAs
   // well and FP8 MFMAs poorly. LDS operands are read three PV MFMAs (V^T) or one S MFMA
   // (K) ahead of use. A wave runs wave_tiles + 1 active iterations: the last one is a
@@ -569,8 +569,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
       ka = k_operand(kl, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (it + 2 < n_tiles) issue(it + 2, true);
-    if (it + 1 < n_tiles) issue(it + 1, false);
+    if (!active) {
+      if (it + 2 < n_tiles) issue(it + 2, true);
+      if (it + 1 < n_tiles) issue(it + 1, false);
+    }
 
     if (active) {
       const int kt = it * kBN;
@@ -649,6 +651,11 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void prefill_fp8_kernel(Prefill
       }
       __builtin_amdgcn_sched_barrier(0);
       s_n[1] = mfma_f8(ka, qf[2], s_n[1]);
+      // the loads of K(it+2) and V(it+1), issued once the S MFMAs are under way (at the
+      // top of the iteration, before the operand reads had landed, 1-2 % slower; spread
+      // over the S and PV MFMAs wave by wave, 4-5 % slower)
+      if (it + 2 < n_tiles) issue(it + 2, true);
+      if (it + 1 < n_tiles) issue(it + 1, false);
       __builtin_amdgcn_sched_barrier(0);
       // PV MFMA j covers dims 32 (j & 3) .. + 31 and key chunk q = j >> 2 (b2 = q >> 1,
       // ck = q & 1); softmax pair j & 3 of chunk q follows it
