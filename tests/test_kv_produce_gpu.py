@@ -96,8 +96,11 @@ def _check(B, n_tokens, heads, seed, sample=None):
     return k8, v8
 
 
-@pytest.mark.parametrize("n_tokens", [1, 127, 128, 129, 300])
+@pytest.mark.parametrize("n_tokens", [1, 127, 128, 129, 300, 1000])
 def test_kv_produce_ragged(gpu_lib, n_tokens):
+    # 1..129 tokens: one 256-token tile (work items in grid order); 300: two tiles, 24
+    # items (each XCD a contiguous range); 1000: four tiles, the last of 232 tokens (each
+    # XCD half of the heads over a quarter of the tiles)
     _check(gpu_lib, n_tokens, 12, 40 + n_tokens)
 
 
