@@ -373,20 +373,31 @@ def main(argv=None):
     log(f"[bench] dynamic quant {dyn_ms * 1e3:.1f} us ({dyn_bytes / dyn_ms / 1e6:.0f} GB/s, "
         f"{dyn_ms / quant_ms:.2f}x the static quantizer)")
     if chunked:
-        kernels["chunked_prefill_ms"] = round(prefill_ms, 4)
-        kernels["pipeline_ms"] = round(quant_ms + prefill_ms, 4)
-        # the same attention as one unsegmented bottom-right causal call
-        single_ms, _ = event_ms(torch, prefill_single(prepare=True), reps, stream)
-        kernels["unsegmented_prefill_ms"] = round(single_ms, 4)
-        kernels["unsegmented_TFLOPs"] = round(flop / (single_ms * 1e-3) / 1e12, 2)
-        # the plan as the workload states it (every context segment its own call, bf16
-        # partials, one public merge per query chunk), through the public calls
+        # the same attention as one unsegmented bottom-right causal call, and the plan as the
+        # workload states it (every context segment its own call, bf16 partials, one public
+        # merge per query chunk) through the public calls. The three are timed once more in
+        # the reverse order and each keeps its better mean: the first of a run's timings
+        # tends to be the slowest, which would favour whichever comes later.
+        single_fn = prefill_single(prepare=True)
+        single_ms, _ = event_ms(torch, single_fn, reps, stream)
         p_out = torch.empty_like(out)
         p_lse = torch.empty_like(lse)
         run_plan, n_pf, n_mg = public_plan(torch, B, codes, descales, wl.softmax_scale,
                                            wl.segment_len, wl.total_q, wl.total_k, p_out, p_lse)
         run_plan()
-        plan_ms, _ = event_ms(torch, run_plan, max(3, reps // 4), stream)
+        plan_reps = max(3, reps // 4)
+        plan_ms, _ = event_ms(torch, run_plan, plan_reps, stream)
+        plan_ms = min(plan_ms, event_ms(torch, run_plan, plan_reps, stream)[0])
+        single_ms = min(single_ms, event_ms(torch, single_fn, reps, stream)[0])
+        again_ms, again_min = event_ms(torch, prefill(prepare=True), reps, stream)
+        if again_ms < prefill_ms:
+            prefill_ms, prefill_min = again_ms, again_min
+            achieved = flop / (prefill_ms * 1e-3) / 1e12
+        log(f"[bench] {what}, best of two timings: {prefill_ms:.3f} ms = {achieved:.1f} TFLOP/s")
+        kernels["chunked_prefill_ms"] = round(prefill_ms, 4)
+        kernels["pipeline_ms"] = round(quant_ms + prefill_ms, 4)
+        kernels["unsegmented_prefill_ms"] = round(single_ms, 4)
+        kernels["unsegmented_TFLOPs"] = round(flop / (single_ms * 1e-3) / 1e12, 2)
         kernels["public_segment_plan"] = {
             "ms": round(plan_ms, 4), "TFLOPs": round(flop / (plan_ms * 1e-3) / 1e12, 2),
             "prefill_launches": n_pf, "merge_launches": n_mg}
