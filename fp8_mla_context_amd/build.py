@@ -5,8 +5,10 @@ The library lands in ``fp8_mla_context_amd/lib/libmla_fp8.so``. Two build varian
 the FP8 prefill's PV arithmetic land beside it, with the same exports:
 ``libmla_fp8_pv1.so`` (P rounded once to E4M3, PV on the FP8 MFMA) and
 ``libmla_fp8_pv2.so`` (P in two E4M3 terms, PV on the FP8 MFMA); the default library
-rounds P once to bf16 and runs PV on the bf16 MFMA. Sources compile to objects in
-parallel; only the prefill source differs between the variants.
+rounds P once to bf16 and runs PV on the bf16 MFMA. The default library also holds the
+prefill source built with 4-wave workgroups of 128 rows, for grids of at most one 256-row
+workgroup per CU. Sources compile to objects in parallel; only the prefill source differs
+between the variants.
 """
 
 from __future__ import annotations
@@ -30,6 +32,9 @@ SOURCES = ["abi.hip", "quant_static.hip", "merge_lse.hip", "prefill_fp8.hip", "p
 VARIANT_SOURCE = "prefill_fp8.hip"
 # library suffix -> extra flags of the prefill source
 VARIANTS = {"": [], "_pv1": ["-DMLA_PV_MODE=1"], "_pv2": ["-DMLA_PV_MODE=2"]}
+# the default library also holds the prefill source built with 4-wave workgroups, which
+# its launcher uses for grids of at most one workgroup per CU
+SMALL_GRID_FLAGS = ["-DMLA_PREFILL_WAVES=4", "-DMLA_PREFILL_SMALL_GRID"]
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
 HIP_FLAGS = [
@@ -80,6 +85,8 @@ def build(verbose: bool = False, extra_flags=(), out_path: str = LIB_PATH,
     for suffix, flags in wanted.items():
         obj = os.path.join(obj_dir, VARIANT_SOURCE.replace(".hip", suffix + ".o"))
         jobs[obj] = base + flags + ["-o", obj, os.path.join(CSRC, VARIANT_SOURCE)]
+    small_obj = os.path.join(obj_dir, VARIANT_SOURCE.replace(".hip", "_4w.o"))
+    jobs[small_obj] = base + SMALL_GRID_FLAGS + ["-o", small_obj, os.path.join(CSRC, VARIANT_SOURCE)]
     with ThreadPoolExecutor(max(1, min(len(jobs), os.cpu_count() or 1, 8))) as ex:
         for f in [ex.submit(_run, cmd, verbose) for cmd in jobs.values()]:
             f.result()
@@ -89,6 +96,8 @@ def build(verbose: bool = False, extra_flags=(), out_path: str = LIB_PATH,
         path = variant_path(suffix, out_path)
         tmp = path + ".tmp"
         objs = common + [os.path.join(obj_dir, VARIANT_SOURCE.replace(".hip", suffix + ".o"))]
+        if suffix == "":
+            objs.append(small_obj)
         _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
         os.replace(tmp, path)
     return out_path

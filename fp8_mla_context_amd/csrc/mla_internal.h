@@ -14,6 +14,8 @@ int fail(int status, const char* fmt, ...);
 int ok();
 // Maps the last HIP launch error to a status.
 int check_launch(const char* what);
+// Compute units of the current device (queried once per device; 256 if the query fails).
+int cu_count();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -90,6 +92,8 @@ struct PrefillSegment {
   float* lse;
 };
 int prefill_launch(const PrefillArgs& a, hipStream_t stream);
+// the same launch on 4-wave workgroups of 128 rows (the library's second prefill build)
+int prefill_launch_small(const PrefillArgs& a, hipStream_t stream);
 // one launch over n segments for the query rows of a (a.batch == 1, no cu_seqlens; a.k/a.v
 // hold all keys, a.total_k of them; a.causal is ignored; a.out and a.lse are the merged
 // result when a.counters is set, else ignored)

@@ -8,7 +8,8 @@ block, so every query tile and wave of the launch, with the row within the block
 spread over all lanes); and GPU-side
 invariants (run-to-run bitwise determinism, permutation of packed sequences,
 exact power-of-two V scaling, V = ones); a lazy rescale forced on every tile and
-extreme softmax scales.
+extreme softmax scales; and the 4-wave kernel that small grids run, bitwise against the
+8-wave one on every small case.
 """
 
 import dataclasses
@@ -80,6 +81,26 @@ def test_prefill_small_cases(gpu_lib, case):
     name, lq, lk, causal, heads = CASES[case]
     wl = make_random(100 + case, lq, lk, causal=causal, heads=heads, outliers=True)
     _check(gpu_lib, wl, label=name)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)), ids=[c[0] for c in CASES])
+def test_small_grid_kernel_matches_the_8_wave_kernel(gpu_lib, case, monkeypatch):
+    """Grids of at most one 256-row workgroup per CU run on 4-wave workgroups of 128 rows
+    (every case above does); with MLA_FP8_PREFILL_SMALL_GRID=0 the same call runs the
+    8-wave kernel. Each query row takes the same arithmetic in both (one wave of 32 rows,
+    the same tiles in the same order), so the outputs and LSEs are bitwise equal."""
+    B = gpu_lib
+    name, lq, lk, causal, heads = CASES[case]
+    wl = make_random(100 + case, lq, lk, causal=causal, heads=heads, outliers=True)
+    ds = oracle_descales(wl)
+    dcodes = [dev(c) for c in oracle_codes(wl, ds)]
+    dds = [dev(d) for d in ds]
+    monkeypatch.delenv("MLA_FP8_PREFILL_SMALL_GRID", raising=False)
+    out4, lse4 = (host(x) for x in gpu_prefill(B, wl, dcodes, dds))
+    monkeypatch.setenv("MLA_FP8_PREFILL_SMALL_GRID", "0")
+    out8, lse8 = (host(x) for x in gpu_prefill(B, wl, dcodes, dds))
+    assert np.array_equal(out4, out8), name
+    assert np.array_equal(lse4.view(np.uint32), lse8.view(np.uint32)), name
 
 
 def test_prefill_c1_full_pipeline(gpu_lib):
