@@ -78,6 +78,8 @@ struct PrefillArgs {
   // bf16 result
   int64_t seg_lse_stride = 0;
   int32_t* counters = nullptr;
+  // the caller's max_seqlen_k with cu_seqlens over several sequences (0: not given)
+  int32_t max_seqlen_k = 0;
 };
 
 // One context segment of a multi-segment launch: the same query rows attend keys

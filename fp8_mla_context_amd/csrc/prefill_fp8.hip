@@ -1022,14 +1022,28 @@ int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   const int64_t blocks = n_m * a.batch * a.n_heads;
   if (blocks >= (1ll << 31)) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
 #if MLA_PV_MODE == 0
-  // A grid of at most one workgroup per CU runs as 4-wave workgroups of 128 rows (twice
-  // the workgroups, two per CU, bit-identical results): measured 7-17 % faster for single
-  // sequences of 1K-4K tokens at 12 heads, while on full grids the 8-wave workgroups are
-  // up to 8 % faster. MLA_FP8_PREFILL_SMALL_GRID=0 in the environment keeps every grid
-  // on the 8-wave kernel.
+  // A grid of at most one workgroup per CU whose heaviest workgroup sets the time runs as
+  // 4-wave workgroups of 128 rows (twice the workgroups, bit-identical results), which
+  // halves that workgroup: causal calls whose first query tile sees at most half the keys
+  // of the last (measured 6-17 % faster for single sequences of 1K-5K tokens at 12 heads).
+  // Where every tile sees about the same keys (4K queries at the end of a 69K-token
+  // context) the 8-wave kernel is 11 % faster, as it is on full grids (up to 8 %).
+  // MLA_FP8_PREFILL_SMALL_GRID in the environment: 0 keeps every grid on the 8-wave
+  // kernel, 1 sends every grid of at most one workgroup per CU to the 4-wave kernel.
   if (blocks <= cu_count()) {
     const char* env = getenv("MLA_FP8_PREFILL_SMALL_GRID");
-    if (env == nullptr || env[0] != '0') return prefill_launch_small(a, stream);
+    bool small = false;
+    if (env != nullptr && env[0] == '1') {
+      small = true;
+    } else if (env == nullptr || env[0] != '0') {
+      // one sequence (the call's totals), or the longest sequences of a packed batch
+      const int64_t lq = a.batch > 1 ? a.max_seqlen_q : a.total_q;
+      const int64_t lk = a.batch > 1 ? a.max_seqlen_k : a.total_k;
+      const int64_t first = std::min<int64_t>(  // keys of the first query tile
+          lk, std::max<int64_t>(0, std::min<int64_t>(lq, kBM) + lk - lq));
+      small = a.causal != 0 && lk > 0 && lk >= 2 * first;
+    }
+    if (small) return prefill_launch_small(a, stream);
   }
 #endif
   prm.xcd_order = (a.batch == 1 && a.n_heads % 4 == 0 && n_m % 2 == 0) ? 1 : 0;
@@ -1117,6 +1131,7 @@ extern "C" int mla_fp8_prefill_varlen(const void* q, const void* k, const void* 
   mla::PrefillArgs a{q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, total_q, total_k,
                      n_heads, descale_q, descale_k, descale_v, softmax_scale, causal, out, 0, lse,
                      lse_stride};
+  a.max_seqlen_k = max_seqlen_k;
   return mla::prefill_launch(a, static_cast<hipStream_t>(stream));
 }
 

@@ -85,17 +85,17 @@ def test_prefill_small_cases(gpu_lib, case):
 
 @pytest.mark.parametrize("case", range(len(CASES)), ids=[c[0] for c in CASES])
 def test_small_grid_kernel_matches_the_8_wave_kernel(gpu_lib, case, monkeypatch):
-    """Grids of at most one 256-row workgroup per CU run on 4-wave workgroups of 128 rows
-    (every case above does); with MLA_FP8_PREFILL_SMALL_GRID=0 the same call runs the
-    8-wave kernel. Each query row takes the same arithmetic in both (one wave of 32 rows,
-    the same tiles in the same order), so the outputs and LSEs are bitwise equal."""
+    """Every case above is a grid of at most one 256-row workgroup per CU: with
+    MLA_FP8_PREFILL_SMALL_GRID=1 it runs on the 4-wave workgroups of 128 rows, with 0 on
+    the 8-wave kernel. Each query row takes the same arithmetic in both (one wave of 32
+    rows, the same tiles in the same order), so the outputs and LSEs are bitwise equal."""
     B = gpu_lib
     name, lq, lk, causal, heads = CASES[case]
     wl = make_random(100 + case, lq, lk, causal=causal, heads=heads, outliers=True)
     ds = oracle_descales(wl)
     dcodes = [dev(c) for c in oracle_codes(wl, ds)]
     dds = [dev(d) for d in ds]
-    monkeypatch.delenv("MLA_FP8_PREFILL_SMALL_GRID", raising=False)
+    monkeypatch.setenv("MLA_FP8_PREFILL_SMALL_GRID", "1")
     out4, lse4 = (host(x) for x in gpu_prefill(B, wl, dcodes, dds))
     monkeypatch.setenv("MLA_FP8_PREFILL_SMALL_GRID", "0")
     out8, lse8 = (host(x) for x in gpu_prefill(B, wl, dcodes, dds))
