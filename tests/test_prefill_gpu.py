@@ -2,7 +2,8 @@
 
 Element-wise on small shapes that span several 256-row query tiles and
 64-key tiles with ragged tails (causal and non-causal, Lq != Lk both ways,
-empty sequences, sequences without keys, both block orders); the full small workloads; 1,024 rows of the 32K-token
+empty sequences, sequences without keys, both block orders, 204 packed sequences);
+the full small workloads; 1,024 rows of the 32K-token
 causal workload in the launch configuration the benchmark times (one in every 32-row
 block, so every query tile and wave of the launch, with the row within the block
 spread over all lanes); and GPU-side
@@ -101,6 +102,20 @@ def test_small_grid_kernel_matches_the_8_wave_kernel(gpu_lib, case, monkeypatch)
     out8, lse8 = (host(x) for x in gpu_prefill(B, wl, dcodes, dds))
     assert np.array_equal(out4, out8), name
     assert np.array_equal(lse4.view(np.uint32), lse8.view(np.uint32)), name
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_many_short_sequences(gpu_lib, causal):
+    """200 packed sequences of 0-40 query tokens plus four of 200-300 (key lengths drawn
+    separately when non-causal): the (sequence, head) pairs of every query tile index in
+    their rotated order, most of the grid's workgroups past a short sequence's end, and
+    sequences without queries or keys."""
+    rng = np.random.default_rng(77 if causal else 78)
+    lq = np.concatenate([rng.integers(0, 41, 200), [200, 256, 257, 300]])
+    rng.shuffle(lq)
+    lk = None if causal else rng.integers(0, 60, lq.shape[0])
+    wl = make_random(300 + int(causal), lq, lk, causal=causal, heads=12, outliers=True)
+    _check(gpu_lib, wl, label=f"many_short_{'causal' if causal else 'noncausal'}")
 
 
 def test_prefill_c1_full_pipeline(gpu_lib):
