@@ -6,8 +6,8 @@ the FP8 prefill's PV arithmetic land beside it, with the same exports:
 ``libmla_fp8_pv1.so`` (P rounded once to E4M3, PV on the FP8 MFMA) and
 ``libmla_fp8_pv2.so`` (P in two E4M3 terms, PV on the FP8 MFMA); the default library
 rounds P once to bf16 and runs PV on the bf16 MFMA. The default library also holds the
-prefill source built with 4-wave workgroups of 128 rows, for causal grids of at most one
-256-row workgroup per CU whose query tiles see unequal key ranges. Sources compile to objects in parallel; only the prefill source differs
+prefill source built with 4-wave workgroups of 128 rows, for grids too small to fill the
+chip (see prefill_launch). Sources compile to objects in parallel; only the prefill source differs
 between the variants.
 """
 

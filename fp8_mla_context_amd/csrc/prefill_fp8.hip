@@ -1022,15 +1022,19 @@ int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   const int64_t blocks = n_m * a.batch * a.n_heads;
   if (blocks >= (1ll << 31)) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
 #if MLA_PV_MODE == 0
-  // A grid of at most one workgroup per CU whose heaviest workgroup sets the time runs as
-  // 4-wave workgroups of 128 rows (twice the workgroups, bit-identical results), which
-  // halves that workgroup: causal calls whose first query tile sees at most half the keys
-  // of the last (measured 6-17 % faster for single sequences of 1K-5K tokens at 12 heads).
-  // Where every tile sees about the same keys (4K queries at the end of a 69K-token
-  // context) the 8-wave kernel is 11 % faster, as it is on full grids (up to 8 %).
+  // Grids that leave CUs idle run as 4-wave workgroups of 128 rows (twice the workgroups,
+  // bit-identical results) when that measured faster: (a) at most one workgroup per two
+  // CUs, so that every 4-wave workgroup has a CU to itself (1K-2.5K queries at 12 heads,
+  // causal or not, and short query chunks over long contexts: 14-19 % faster); (b) at
+  // most one workgroup per CU in a causal call whose first query tile sees at most half
+  // the keys of the last, where the heaviest workgroup sets the time and 128-row
+  // workgroups halve it (single sequences of 1K-5K tokens: 6-17 %). Beyond (a), equal key
+  // ranges run faster on the 8-wave kernel (4K queries at the end of a 69K-token context:
+  // 11 %; 3K-4K non-causal queries: 7-8 %), as do full grids (up to 8 %).
   // MLA_FP8_PREFILL_SMALL_GRID in the environment: 0 keeps every grid on the 8-wave
   // kernel, 1 sends every grid of at most one workgroup per CU to the 4-wave kernel.
-  if (blocks <= cu_count()) {
+  const int cus = cu_count();
+  if (blocks <= cus) {
     const char* env = getenv("MLA_FP8_PREFILL_SMALL_GRID");
     bool small = false;
     if (env != nullptr && env[0] == '1') {
@@ -1041,7 +1045,7 @@ int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
       const int64_t lk = a.batch > 1 ? a.max_seqlen_k : a.total_k;
       const int64_t first = std::min<int64_t>(  // keys of the first query tile
           lk, std::max<int64_t>(0, std::min<int64_t>(lq, kBM) + lk - lq));
-      small = a.causal != 0 && lk > 0 && lk >= 2 * first;
+      small = 2 * blocks <= cus || (a.causal != 0 && lk > 0 && lk >= 2 * first);
     }
     if (small) return prefill_launch_small(a, stream);
   }
