@@ -1022,32 +1022,40 @@ int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
   const int64_t blocks = n_m * a.batch * a.n_heads;
   if (blocks >= (1ll << 31)) return fail(MLA_ERR_UNSUPPORTED, "grid too large");
 #if MLA_PV_MODE == 0
-  // Grids that leave CUs idle run as 4-wave workgroups of 128 rows (twice the workgroups,
-  // bit-identical results) when that measured faster: (a) at most one workgroup per two
-  // CUs, so that every 4-wave workgroup has a CU to itself (1K-2.5K queries at 12 heads,
-  // causal or not, and short query chunks over long contexts: 14-19 % faster); (b) at
-  // most one workgroup per CU in a causal call whose first query tile sees at most half
-  // the keys of the last, where the heaviest workgroup sets the time and 128-row
-  // workgroups halve it (single sequences of 1K-5K tokens: 6-17 %). Beyond (a), equal key
-  // ranges run faster on the 8-wave kernel (4K queries at the end of a 69K-token context:
-  // 11 %; 3K-4K non-causal queries: 7-8 %), as do full grids (up to 8 %).
-  // MLA_FP8_PREFILL_SMALL_GRID in the environment: 0 keeps every grid on the 8-wave
-  // kernel, 1 sends every grid of at most one workgroup per CU to the 4-wave kernel.
-  const int cus = cu_count();
-  if (blocks <= cus) {
+  // Grids that leave CUs idle, or whose workgroups differ much in length, run as 4-wave
+  // workgroups of 128 rows (twice the workgroups, bit-identical results) where that
+  // measured faster: (a) at most one workgroup per two CUs, so that every 4-wave workgroup
+  // has a CU to itself (1K-2.5K queries at 12 heads, causal or not, and short query chunks
+  // over long contexts: 14-19 % faster); (b) at most one workgroup per CU in a causal call
+  // whose first query tile sees at most half the keys of the last, where the heaviest
+  // workgroup sets the time and 128-row workgroups halve it (single sequences of 1K-5K
+  // tokens: 6-17 %); (c) packed sequences of unequal lengths, estimated from the grid
+  // being more than a quarter padding (query tiles past a shorter sequence's end), where
+  // the smaller workgroups balance the CUs better (2-10 %; the 8-sequence C2 mix 5 %).
+  // Beyond these the 8-wave kernel is faster: 4K queries at the end of a 69K-token
+  // context 11 %, 3K-4K non-causal queries 7-8 %, full grids of equal sequences up to 8 %.
+  // MLA_FP8_PREFILL_SMALL_GRID in the environment: 0 keeps every call on the 8-wave
+  // kernel, 1 also sends every grid of at most one workgroup per CU to the 4-wave kernel.
+  {
     const char* env = getenv("MLA_FP8_PREFILL_SMALL_GRID");
-    bool small = false;
-    if (env != nullptr && env[0] == '1') {
-      small = true;
-    } else if (env == nullptr || env[0] != '0') {
-      // one sequence (the call's totals), or the longest sequences of a packed batch
-      const int64_t lq = a.batch > 1 ? a.max_seqlen_q : a.total_q;
-      const int64_t lk = a.batch > 1 ? a.max_seqlen_k : a.total_k;
-      const int64_t first = std::min<int64_t>(  // keys of the first query tile
-          lk, std::max<int64_t>(0, std::min<int64_t>(lq, kBM) + lk - lq));
-      small = 2 * blocks <= cus || (a.causal != 0 && lk > 0 && lk >= 2 * first);
+    if (env == nullptr || env[0] != '0') {
+      const int cus = cu_count();
+      bool small = false;
+      if (blocks <= cus) {
+        // one sequence (the call's totals), or the longest sequences of a packed batch
+        const int64_t lq = a.batch > 1 ? a.max_seqlen_q : a.total_q;
+        const int64_t lk = a.batch > 1 ? a.max_seqlen_k : a.total_k;
+        const int64_t first = std::min<int64_t>(  // keys of the first query tile
+            lk, std::max<int64_t>(0, std::min<int64_t>(lq, kBM) + lk - lq));
+        small = (env != nullptr && env[0] == '1') || 2 * blocks <= cus ||
+                (a.causal != 0 && lk > 0 && lk >= 2 * first);
+      }
+      // workgroups with rows: about (total_q / 256 + batch / 2) per head
+      if (!small && a.batch > 1)
+        small = (a.total_q + static_cast<int64_t>(kBM / 2) * a.batch) * a.n_heads <
+                static_cast<int64_t>(kBM) * 3 / 4 * blocks;
+      if (small) return prefill_launch_small(a, stream);
     }
-    if (small) return prefill_launch_small(a, stream);
   }
 #endif
   prm.xcd_order = (a.batch == 1 && a.n_heads % 4 == 0 && n_m % 2 == 0) ? 1 : 0;

@@ -190,11 +190,13 @@ int mla_fp8_kv_produce(const void* c_kv, int64_t c_kv_stride, const void* k_pe,
  *   head_dim_qk/head_dim_v other than 192/128 -> MLA_ERR_UNSUPPORTED.
  *   Any n_heads >= 1 is accepted (heads are independent; the workloads use 12).
  *   Grids of at most one 256-row workgroup per two CUs (ceil(max_seqlen_q / 256) * batch
- *   * n_heads <= half the device's CU count), and causal grids of at most one per CU whose
- *   first query tile sees at most half the keys of the last, run on 128-row workgroups;
- *   results are bitwise the same. The environment variable MLA_FP8_PREFILL_SMALL_GRID,
- *   read at each call: 0 keeps every grid on 256-row workgroups, 1 runs every grid of at
- *   most one 256-row workgroup per CU on 128-row ones.
+ *   * n_heads <= half the device's CU count), causal grids of at most one per CU whose
+ *   first query tile sees at most half the keys of the last, and packed batches whose
+ *   grid is more than a quarter padding (sequences of unequal lengths) run on 128-row
+ *   workgroups; results are bitwise the same. The environment variable
+ *   MLA_FP8_PREFILL_SMALL_GRID, read at each call: 0 keeps every call on 256-row
+ *   workgroups, 1 also runs every grid of at most one 256-row workgroup per CU on
+ *   128-row ones.
  */
 int mla_fp8_prefill_varlen(const void* q, const void* k, const void* v,
                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

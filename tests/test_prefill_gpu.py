@@ -141,6 +141,23 @@ def test_prefill_c2_full(gpu_lib):
     _check(gpu_lib, make_workload("C2"), label="C2")
 
 
+def test_c2_runs_the_4_wave_kernel_bitwise_like_the_8_wave_one(gpu_lib, monkeypatch):
+    """The C2 mix (8 sequences of 808-3,975 tokens, a third of its grid padding) runs on
+    128-row workgroups; with MLA_FP8_PREFILL_SMALL_GRID=0 on the 8-wave kernel. Bitwise
+    equal outputs and LSEs."""
+    B = gpu_lib
+    wl = make_workload("C2")
+    ds = oracle_descales(wl)
+    dcodes = [dev(c) for c in oracle_codes(wl, ds)]
+    dds = [dev(d) for d in ds]
+    monkeypatch.delenv("MLA_FP8_PREFILL_SMALL_GRID", raising=False)
+    out4, lse4 = (host(x) for x in gpu_prefill(B, wl, dcodes, dds))
+    monkeypatch.setenv("MLA_FP8_PREFILL_SMALL_GRID", "0")
+    out8, lse8 = (host(x) for x in gpu_prefill(B, wl, dcodes, dds))
+    assert np.array_equal(out4, out8)
+    assert np.array_equal(lse4.view(np.uint32), lse8.view(np.uint32))
+
+
 def test_prefill_c3_sampled_rows(gpu_lib):
     """32K causal at full size, same launch as the benchmark; oracle on 1,024 stratified rows
     (one per 32-row wave block of every 256-row query tile) plus the edges."""
