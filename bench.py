@@ -459,8 +459,9 @@ def main(argv=None):
             log(f"[bench] split-KV over {seg}-key segments (chunked call, merge in the launch): "
                 f"{split_ms:.3f} ms = {flop / (split_ms * 1e-3) / 1e12:.1f} TFLOP/s")
             del ws, s_out, s_lse
-        # the varlen grid: query tiles of the longest sequence x sequences x heads; the
-        # workgroups of shorter sequences past their last row exit at once
+        # the 256-row varlen grid: query tiles of the longest sequence x sequences x heads;
+        # the workgroups of shorter sequences past their last row exit at once (a grid more
+        # than a quarter empty runs as twice as many 128-row workgroups)
         lens = np.diff(wl.cu_seqlens_q)
         grid = int((int(lens.max()) + 255) // 256) * len(lens) * heads
         busy = int(np.sum((lens + 255) // 256)) * heads
