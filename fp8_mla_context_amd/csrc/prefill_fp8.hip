@@ -1050,8 +1050,9 @@ int prefill_launch(const PrefillArgs& a, hipStream_t stream) {
         small = (env != nullptr && env[0] == '1') || 2 * blocks <= cus ||
                 (a.causal != 0 && lk > 0 && lk >= 2 * first);
       }
-      // workgroups with rows: about (total_q / 256 + batch / 2) per head
-      if (!small && a.batch > 1)
+      // workgroups with rows: about (total_q / 256 + batch / 2) per head; the 128-row grid
+      // must stay within the launch limit
+      if (!small && a.batch > 1 && 2 * blocks < (1ll << 31))
         small = (a.total_q + static_cast<int64_t>(kBM / 2) * a.batch) * a.n_heads <
                 static_cast<int64_t>(kBM) * 3 / 4 * blocks;
       if (small) return prefill_launch_small(a, stream);
