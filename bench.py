@@ -55,12 +55,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def record_counters(dirs, workload: str) -> dict:
+def record_counters(dirs, workload: str, path: str = None) -> dict:
     """Build the per-launch counter record of the prefill from rocprofv3 `--pmc` output
     directories (one per pass, csv format) of a run with --copy-probe-mib 1024, and write
     it to profiles/prefill_<workload>_counters.json. Counter values are summed over their
     dimensions per dispatch and averaged over dispatches; FETCH_SIZE and WRITE_SIZE are
-    scaled by what they read for the elementwise probe, which moves 1 GiB each way."""
+    scaled by what they read for the elementwise probe, which moves 1 GiB each way. `path`
+    overrides where the record is written."""
     import csv
     import glob
     import re as _re
@@ -109,16 +110,18 @@ def record_counters(dirs, workload: str) -> dict:
                     ("SQ_VALU_MFMA_COEXEC_CYCLES", "valu_mfma_coexec_cycles_per_simd")):
         if cn in v:
             rec[key] = int(round(v[cn] / 1024))  # 256 CUs x 4 SIMDs
-    path = os.path.join(ROOT, "profiles", f"prefill_{workload.lower()}_counters.json")
+    if path is None:
+        path = os.path.join(ROOT, "profiles", f"prefill_{workload.lower()}_counters.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     return rec
 
 
-def load_counters(kernel_hash: str, workload: str):
+def load_counters(kernel_hash: str, workload: str, path: str = None):
     """Per-launch counter record of the prefill (HBM bytes, GPU clock cycles) for this
     workload, if it was taken on the current kernel sources; else an empty dict."""
-    path = os.path.join(ROOT, "profiles", f"prefill_{workload.lower()}_counters.json")
+    if path is None:
+        path = os.path.join(ROOT, "profiles", f"prefill_{workload.lower()}_counters.json")
     if not os.path.exists(path):
         return {}
     with open(path) as f:
