@@ -183,6 +183,16 @@ __device__ __forceinline__ void store16_agent(float* ptr, float4 v) {
 __device__ __forceinline__ float load_agent(const float* ptr) {
   return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// eight consecutive floats (32-byte aligned) as four agent-coherent 8-byte loads
+__device__ __forceinline__ void load8_agent(const float* ptr, float (&x)[8]) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(ptr);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t v = __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    x[2 * i] = __uint_as_float(static_cast<uint32_t>(v));
+    x[2 * i + 1] = __uint_as_float(static_cast<uint32_t>(v >> 32));
+  }
+}
 
 // S^T block for one tile: two 32-key blocks, K-dim 192 = 3 x 64
 __device__ __forceinline__ void qk_tile(const uint8_t* kl, int col, int g, const v8i qf[3],
@@ -212,6 +222,8 @@ __device__ __forceinline__ int v_swizzle(int key) { return (key & 3) | (((key >>
 //   L = ln sum_s exp(L_s),  out = sum_s exp(L_s - L) * out_s   (all L_s = -inf: 0, -inf)
 // with the arithmetic of the separate merge kernel (same order over s), reading the
 // partials with agent-coherent loads issued after the counter returned.
+constexpr int kMergeBatch = 4;  // segments whose partials a merge loads at once
+
 template <int kNSeg>
 __device__ __forceinline__ void merge_on_last_arrival(const PrefillParams& p,
                                                       const SegTable<kNSeg>& st, int h, int m_tile,
@@ -229,22 +241,74 @@ __device__ __forceinline__ void merge_on_last_arrival(const PrefillParams& p,
   if (tid == 0)  // ready for the next launch on this stream
     __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int H = p.n_heads;
+  const int n = st.n;
   for (int item = tid; item < rows * 16; item += kThreads) {
     const int64_t row = row0 + (item >> 4);
     const int c8 = item & 15;
     const int64_t li = static_cast<int64_t>(h) * p.seg_lse_stride + row;
-    float m = -INFINITY;
-    for (int s = 0; s < st.n; ++s) m = fmaxf(m, load_agent(st.e[s].lse + li));
+    const int64_t eo = (row * H + h) * kDv + 8 * c8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float tot = 0.f;
-    const int64_t eo = (row * H + h) * kDv + 8 * c8;
-    if (m != -INFINITY) {
-      for (int s = 0; s < st.n; ++s) {
-        const float w = __expf(load_agent(st.e[s].lse + li) - m);  // 0 for an empty segment
-        tot += w;
-        const float* src = static_cast<const float*>(st.e[s].out) + eo;
+    float m = -INFINITY;
+    // The loads of up to kMergeBatch segments are issued together, so that a row waits
+    // for memory once when its segments fit one batch, else twice per batch (the LSEs for
+    // the maximum, then LSEs and partials), rather than twice per segment; the arithmetic
+    // and its order over s are unchanged.
+    if (n <= kMergeBatch) {
+      float lv[kMergeBatch], x[kMergeBatch][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += w * load_agent(src + i);
+      for (int j = 0; j < kMergeBatch; ++j) {
+        lv[j] = -INFINITY;
+        if (j < n) {
+          lv[j] = load_agent(st.e[j].lse + li);
+          load8_agent(static_cast<const float*>(st.e[j].out) + eo, x[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j)
+        if (j < n) m = fmaxf(m, lv[j]);
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+          if (j < n) {
+            const float w = __expf(lv[j] - m);  // 0 for an empty segment
+            tot += w;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += w * x[j][i];
+          }
+        }
+      }
+    } else {
+      for (int s0 = 0; s0 < n; s0 += kMergeBatch) {
+        float lv[kMergeBatch];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j)
+          lv[j] = (s0 + j < n) ? load_agent(st.e[s0 + j].lse + li) : -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j)
+          if (s0 + j < n) m = fmaxf(m, lv[j]);
+      }
+      if (m != -INFINITY) {
+        for (int s0 = 0; s0 < n; s0 += kMergeBatch) {
+          float lv[kMergeBatch], x[kMergeBatch][8];
+#pragma unroll
+          for (int j = 0; j < kMergeBatch; ++j) {
+            lv[j] = -INFINITY;
+            if (s0 + j < n) {
+              lv[j] = load_agent(st.e[s0 + j].lse + li);
+              load8_agent(static_cast<const float*>(st.e[s0 + j].out) + eo, x[j]);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < kMergeBatch; ++j) {
+            if (s0 + j < n) {
+              const float w = __expf(lv[j] - m);  // 0 for an empty segment
+              tot += w;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) acc[i] += w * x[j][i];
+            }
+          }
+        }
       }
     }
     const float inv = (m != -INFINITY) ? 1.0f / tot : 0.0f;
