@@ -9,10 +9,11 @@
 //  * One workgroup = 8 waves = 256 query rows of one (sequence, head); each wave owns
 //    32 rows; one workgroup per CU, two waves per SIMD, so one wave's VALU work fills the
 //    other's MFMA time. Every K/V tile a workgroup loads and converts serves 256 rows
-//    (4-wave workgroups of 128 rows, two per CU, are a build option: 5 % slower on the
-//    32K causal prefill). Workgroups are ordered heaviest first: the flattened block
-//    index walks query tiles from the last (most keys under a causal mask) to the first,
-//    with heads and sequences fastest.
+//    (4-wave workgroups of 128 rows, two per CU, are a second build of this source: 5 %
+//    slower on the 32K causal prefill, faster on grids that leave CUs idle or are mostly
+//    padding, which prefill_launch hands to it). Workgroups are ordered heaviest first:
+//    the flattened block index walks query tiles from the last (most keys under a causal
+//    mask) to the first, with heads and sequences fastest.
 //  * 64-key K tiles and FP8 V tiles live in two LDS buffers each, filled by
 //    global->LDS DMA (global_load_lds_dwordx4, no register staging). K rows are padded to
 //    208 bytes; V rows are 128 bytes with XOR-swizzled 16-byte chunks (see v_swizzle).
@@ -47,7 +48,9 @@
 //    a wave skips tiles past its last visible key; only tiles that cross the
 //    diagonal or the ragged end are masked element-wise.
 //  * Epilogue: out = O * dv / l in bf16 (fp32 for the partials of a chunked pass),
-//    lse = ln2 * (m + log2 l).
+//    lse = ln2 * (m + log2 l). A launch over several key segments merges its own
+//    partials: the last workgroup of each (query tile, head) to finish combines them
+//    (merge_on_last_arrival).
 #include <stdlib.h>
 
 #include <algorithm>
@@ -71,7 +74,8 @@ constexpr int kDqk = 192;
 constexpr int kDv = 128;
 // The library holds this source twice: the default 8-wave build, and a 4-wave build
 // (MLA_PREFILL_SMALL_GRID) that exports only mla::prefill_launch_small, to which the
-// default build hands grids that would leave CUs idle (see prefill_launch).
+// default build hands grids that would leave CUs idle or are mostly padding (see
+// prefill_launch).
 #ifndef MLA_PREFILL_WAVES
 #define MLA_PREFILL_WAVES 8
 #endif
