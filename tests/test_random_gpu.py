@@ -17,7 +17,12 @@ accumulation (error up to 2^-12 of the row's summed |q k| magnitudes) moves near
 outputs by up to about one bf16 ulp: one such draw of the varlen shapes below reached
 0.0286 sigma (1.07 ulp at |out| = 5.8 sigma), where the same arithmetic with exact fp32
 logits gives 0.0122 sigma.
+
+Wider draws: MLA_RANDOM_VARLEN=60 MLA_RANDOM_CHUNKED=40 runs 100 cases (the chunked ones up
+to the 64-part maximum), the default ones first.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -31,10 +36,10 @@ from tests.parity import (assert_attention_parity, attention_errors, bf16_bits_t
 pytestmark = pytest.mark.gpu
 
 
-def _varlen_cases():
+def _varlen_cases(count):
     rng = np.random.default_rng(20261203)
     cases = []
-    for i in range(12):
+    for i in range(count):
         b = int(rng.integers(1, 10))
         heads = int(rng.choice([1, 3, 8, 12]))
         causal = bool(rng.integers(0, 2))
@@ -49,10 +54,10 @@ def _varlen_cases():
     return cases
 
 
-def _chunked_cases():
+def _chunked_cases(count):
     rng = np.random.default_rng(4711)
     cases = []
-    while len(cases) < 10:
+    while len(cases) < count:
         causal = bool(rng.integers(0, 2))
         lq = int(rng.integers(1, 600))
         lk = lq + int(rng.integers(0, 2500)) if causal else int(rng.integers(1, 3000))
@@ -65,8 +70,10 @@ def _chunked_cases():
     return cases
 
 
-VARLEN = _varlen_cases()
-CHUNKED = _chunked_cases()
+# case counts (MLA_RANDOM_VARLEN, MLA_RANDOM_CHUNKED in the environment for a wider run;
+# the default cases are the first of any wider draw)
+VARLEN = _varlen_cases(int(os.environ.get("MLA_RANDOM_VARLEN", "12")))
+CHUNKED = _chunked_cases(int(os.environ.get("MLA_RANDOM_CHUNKED", "10")))
 
 
 def _errors(wl, codes, ds, out, lse, causal, ref_o, ref_l):
