@@ -246,7 +246,8 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=15,
+                    help="untimed steps first: the clock takes about a dozen 32K-token prefills to settle")
     ap.add_argument("--workload", default="C3", choices=["C1", "C2", "C3", "C4", "C5", "NC"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the timed oracle sample")
